@@ -1,0 +1,216 @@
+/* mk.h -- C ABI of the MI355X decode megakernel library (libmk.so).
+ *
+ * One decode step of a decoder-only transformer is lowered once, on the host, into a
+ * static, topologically ordered array of 64-byte task descriptors plus a flat CSR
+ * array of dependency edges ("Mega kernel initial", 1y33.com: sections on the
+ * lowering, the task descriptor and the edge array).  mk_decode_step then runs the
+ * whole step as ONE persistent kernel launch: one workgroup per compute unit pulls
+ * tasks in emission order and starts each one as soon as its own producers have
+ * finished, tracked by per-task readiness counters in device memory -- no grid-wide
+ * barrier ("Megakernels", runhoid.com: "Megakernel iceberg", layer 6, and "Hoid's
+ * approach to megakernels").
+ *
+ * Conventions for every entry point:
+ *   - Return value: 0 on success, a negative MK_ERR_* code on failure.  Nothing throws
+ *     across the ABI.  mk_last_error() returns a thread-local message for the last
+ *     failing call on the calling thread.
+ *   - "device pointer" = memory from hipMalloc (or a PyTorch CUDA/HIP tensor) on the
+ *     current device; "host pointer" = ordinary process memory.
+ *   - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer it passes (weights, KV caches, scratch, tokens,
+ *     positions, logits).  The library never frees caller memory.  The library owns
+ *     the graph object, its host copies of tasks and edges, and its small device
+ *     allocations (descriptor blob, buffer table, readiness counters, control block),
+ *     all released by mk_destroy.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1u
+
+/* ---- error codes ---------------------------------------------------------------- */
+#define MK_OK 0
+#define MK_ERR_ABI (-1)        /* abi_version or struct_size mismatch                  */
+#define MK_ERR_INVALID (-2)    /* a configuration value or argument is out of range    */
+#define MK_ERR_ALIGN (-3)      /* a device pointer is not 16-byte aligned              */
+#define MK_ERR_HIP (-4)        /* a HIP runtime call failed (message has the reason)  */
+#define MK_ERR_NOMEM (-5)      /* host or device allocation failed                    */
+#define MK_ERR_DEVICE (-6)     /* the device status word reports a failure (mk_status) */
+
+/* Device status word (mk_status): 0 = ok; otherwise the top 4 bits hold the kind and
+ * the low 28 bits the index of the task that raised it. */
+#define MK_STATUS_TIMEOUT 0x10000000u      /* a dependency wait exceeded its bound      */
+#define MK_STATUS_BAD_POSITION 0x20000000u /* positions[b] outside [0, kv_len[b])       */
+#define MK_STATUS_BAD_TOKEN 0x30000000u    /* tokens[b] outside [0, vocab)              */
+#define MK_STATUS_KIND_MASK 0xF0000000u
+
+/* ---- task descriptor ("Mega kernel initial", descriptor section) ------------------
+ * 64-byte POD, identical on host and device; buffers are referenced by uint16 index
+ * into the buffer table, never by pointer.  Field offsets: 0,2,4,6,8,12,16,20,26,28,
+ * 32,36,40,44.  Per-op meaning of m/n/k/kv_len/reserved (reserved = per-op scalars):
+ *   GEMV (2):    m = batch rows, n = output columns of the whole matmul, k = inner dim;
+ *                reserved = {col_begin, col_count, I (SILU_MUL: up rows start) or 0};
+ *                in_buf = {x, W, gamma (RMS_NORM_INPUT) | residual (ADD_RESIDUAL) | none}
+ *   ATTENTION_APPEND (7): m = batch, n = head_dim, k = KV head g, kv_len = capacity;
+ *                reserved = {b, first q head, q heads per group, kcache buf, vcache buf}
+ *   ATTENTION_PARTIAL (8): m = chunks of sequence b, n = head_dim, k = g,
+ *                kv_len = chunk size; reserved = {b, first q head, heads, chunk c,
+ *                first partial slot of (b, g)}; in_buf = {q_rot, kcache, vcache}
+ *   ATTENTION_COMBINE (9): as PARTIAL with reserved[3] = 0; in_buf = {partials}
+ *   MEMCPY (1):  embedding gather, m = batch, n = hidden; in_buf = {tokens, E}
+ *   NOP (0):     join node; only the dependency fields are set.
+ * remaining_deps is the in-degree (constant; run-time readiness uses separate
+ * counters).  step is always 0.  config_id selects the body variant: GEMV 0 fp32,
+ * 1 bf16 vector, 2 bf16 MFMA; APPEND/PARTIAL cache dtype (0 f32, 1 bf16); MEMCPY
+ * embedding dtype. */
+typedef struct mk_task {
+  uint16_t op_id;
+  uint16_t config_id;
+  uint16_t step;
+  uint16_t flags;
+  int32_t remaining_deps;
+  int32_t num_dependents;
+  uint32_t dependents_offset;
+  uint16_t in_buf[3];
+  uint16_t out_buf;
+  int32_t m;
+  int32_t n;
+  int32_t k;
+  int32_t kv_len;
+  uint32_t reserved[5];
+} mk_task_t;
+
+/* OpId values and flag bits as listed on the page (OpId table; flags paragraph). */
+enum {
+  MK_OP_NOP = 0, MK_OP_MEMCPY = 1, MK_OP_GEMV = 2, MK_OP_RMSNORM = 3, MK_OP_ATTENTION = 4,
+  MK_OP_MLP = 5, MK_OP_SAMPLE = 6, MK_OP_ATTENTION_APPEND = 7, MK_OP_ATTENTION_PARTIAL = 8,
+  MK_OP_ATTENTION_COMBINE = 9
+};
+enum { MK_FLAG_SILU_MUL = 1, MK_FLAG_ADD_RESIDUAL = 2, MK_FLAG_RMS_NORM_INPUT = 4 };
+
+enum { MK_DTYPE_F32 = 0, MK_DTYPE_BF16 = 1 };
+enum { MK_GEMV_F32 = 0, MK_GEMV_BF16 = 1, MK_GEMV_BF16_MFMA = 2 };
+
+/* ---- model configuration -----------------------------------------------------------
+ * Decoder: per layer qkv = W_qkv * rmsnorm(x, attn_norm); RoPE-append; GQA attention
+ * over the cache; h = x + W_o * att; x' = h + W_down * (silu(gate) * up) with
+ * [gate; up] = W_gate_up * rmsnorm(h, mlp_norm); logits = W_lm * rmsnorm(x, final_norm)
+ * ("Mega kernel initial", graph API section).  Weights are row-major [out, in].
+ * kv_len[b] (host pointer, batch entries, read during the call only) is the attended
+ * length planned for sequence b including the new token; it fixes that sequence's
+ * number of KV chunks.  At run time sequence b attends to slots [0, positions[b]], so
+ * positions[b] + 1 <= kv_len[b] <= kv_capacity. */
+typedef struct mk_model_cfg {
+  uint32_t abi_version; /* MK_ABI_VERSION */
+  uint32_t struct_size; /* sizeof(mk_model_cfg) */
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, batch;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype, kv_dtype; /* MK_DTYPE_* */
+  int32_t gemv_tiles;             /* column tiles per matmul (T) */
+  int32_t kv_chunk;               /* keys per ATTENTION_PARTIAL task */
+  int32_t join_nodes;             /* 1: insert NOP join tasks for shared parent sets */
+  int32_t gemv_config;            /* MK_GEMV_* */
+  int32_t kv_capacity;            /* cache slots per (layer, sequence, KV head) */
+  int32_t reserved0;
+  const int32_t* kv_len;          /* host pointer, [batch] */
+} mk_model_cfg;
+
+/* Weights in canonical order (buffer-table section of the page: append-only, one
+ * index per tensor): [0] embedding [vocab, hidden]; per layer l at 1 + 6 l:
+ * attn_norm [hidden], W_qkv [(Hq + 2 Hkv) hd, hidden], W_o [hidden, Hq hd],
+ * mlp_norm [hidden], W_gate_up [2 I, hidden], W_down [hidden, I]; then final_norm
+ * [hidden] and W_lm [vocab, hidden].  count = 3 + 6 n_layers.  Device pointers in
+ * weight_dtype, each 16-byte aligned. */
+typedef struct mk_weights {
+  uint32_t count;
+  void* const* dev_ptrs; /* host array of device pointers */
+} mk_weights;
+
+typedef struct mk_graph mk_graph;     /* lowered + uploaded graph (device-side state) */
+typedef struct mk_lowered mk_lowered; /* host-only lowering result */
+
+/* Sizes of the lowered graph and of the scratch block the caller must provide.
+ * Host only; touches no GPU. */
+typedef struct mk_plan_info {
+  uint32_t n_tasks;
+  uint32_t n_edges;
+  uint32_t n_buffers;
+  uint32_t n_levels;         /* 1 + max level (level = 1 + max parent level) */
+  uint64_t scratch_bytes;    /* activation scratch for one step */
+  uint64_t kv_layer_bytes;   /* bytes of one layer's K (or V) cache slab */
+} mk_plan_info;
+
+int mk_plan(const mk_model_cfg* cfg, mk_plan_info* out);
+
+/* Host-only lowering (no GPU calls): the descriptor array and CSR edge array that
+ * mk_build_graph would upload.  Arrays stay owned by the mk_lowered object. */
+int mk_lower(const mk_model_cfg* cfg, mk_lowered** out);
+int mk_lowered_tasks(const mk_lowered* g, const mk_task_t** tasks, uint32_t* n);
+int mk_lowered_edges(const mk_lowered* g, const uint32_t** edges, uint32_t* n);
+/* Byte offset and size of activation buffer `buf_index` inside the scratch block
+ * (error for buffers that are not scratch). */
+int mk_lowered_scratch_span(const mk_lowered* g, uint32_t buf_index, uint64_t* offset, uint64_t* bytes);
+void mk_lowered_free(mk_lowered* g);
+
+/* Lower, then upload descriptors + edges (one blob behind a 64-byte header) and the
+ * buffer table to the device, on `stream`.  `scratch_dev` (device pointer, at least
+ * mk_plan().scratch_bytes, 256-byte aligned) holds the step's activations.  The
+ * weights must stay valid for the graph's lifetime. */
+int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scratch_dev,
+                   void* stream, mk_graph** out);
+
+/* Host copies of what mk_build_graph uploaded (library-owned, valid until mk_destroy). */
+int mk_graph_tasks(const mk_graph* g, const mk_task_t** tasks, uint32_t* n);
+int mk_graph_edges(const mk_graph* g, const uint32_t** edges, uint32_t* n);
+
+/* One decode step as ONE persistent-kernel launch, enqueued on `stream` (no host
+ * synchronisation).  Device pointers: tokens_dev int32[batch]; positions_dev
+ * int32[batch]; kcache_dev / vcache_dev [n_layers][batch][n_kv_heads][kv_capacity]
+ * [head_dim] in kv_dtype (slot positions[b] of every layer is overwritten with the new
+ * token's rotated k and its v); logits_dev float32[batch][vocab].  The step reads the
+ * cache slots [0, positions[b]].  Out-of-range positions set the device status
+ * (mk_status) and leave the outputs of the affected sequence undefined. */
+int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
+                   void* kcache_dev, void* vcache_dev, float* logits_dev);
+
+/* The same step with the same task bodies and descriptors, one kernel launch per op
+ * (stream order instead of readiness counters): the per-op-launch baseline. */
+int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
+                          const int32_t* positions_dev, void* kcache_dev, void* vcache_dev,
+                          float* logits_dev);
+
+/* Synchronises `g`'s last stream and reads the device status word (see
+ * MK_STATUS_*).  A non-zero status is cleared and the graph's scheduler state is
+ * reset, so the next step runs normally.  Returns MK_ERR_DEVICE if it was non-zero. */
+int mk_status(mk_graph* g, uint32_t* device_status);
+
+/* Bound on one dependency wait, in ticks of the 100 MHz constant clock
+ * (default 200,000,000 = 2 s).  A wait that exceeds it sets MK_STATUS_TIMEOUT and
+ * the kernel drains instead of hanging. */
+int mk_set_wait_limit(mk_graph* g, uint64_t ticks);
+
+/* Trace mode: when `trace_dev` is non-NULL (device pointer, n_tasks * 4 uint64), the
+ * next mk_decode_step calls record per task {XCC_ID << 32 | HW_ID register, claim
+ * time, ready time (dependency wait over), end time (body done)}, times in ticks of
+ * the constant 100 MHz clock.  NULL turns it off.  The pointer must stay valid while
+ * steps that use it run. */
+int mk_set_trace(mk_graph* g, uint64_t* trace_dev);
+
+/* Number of workgroups the persistent kernel is launched with (one per CU). */
+int mk_graph_grid(const mk_graph* g, uint32_t* workgroups);
+
+void mk_destroy(mk_graph* g);
+const char* mk_last_error(void);
+uint32_t mk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

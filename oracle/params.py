@@ -24,11 +24,9 @@ class GeneratedParams:
     def _flat(self, tid: int, n: int, start: int = 0) -> np.ndarray:
         _, _, _, mean, std, dtype = self.specs[tid]
         if self.backend == "numpy":
-            raw = gen.fill(self.w.seed, tid, n, mean, std, dtype, start=start)
-        else:
-            from synth import native
-            raw = native.cpu_fill_flat(n, start, self.w.seed, tid, mean, std, dtype)
-        return gen.to_f64(raw, dtype)
+            return gen.to_f64(gen.fill(self.w.seed, tid, n, mean, std, dtype, start=start), dtype)
+        from synth import native
+        return native.cpu_fill_flat_f64(n, start, self.w.seed, tid, mean, std, dtype)
 
     def embedding_row(self, token: int) -> np.ndarray:
         H = self.w.hidden

@@ -47,6 +47,22 @@ void synth_fill_flat(void* dst, int dtype, uint64_t n, uint64_t start,
     }
 }
 
+/* Stored values (binary32, or bfloat16 for dtype 1) widened exactly to binary64. */
+void synth_fill_flat_f64(double* dst, int dtype, uint64_t n, uint64_t start,
+                         uint64_t seed, uint64_t tid, double mean, double scale) {
+    uint64_t key = synth_stream_key(seed, tid);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < (int64_t)n; ++j) {
+        float f = (float)draw(key, start + (uint64_t)j, mean, scale);
+        if (dtype == 1) {
+            union { float f; uint32_t u; } c;
+            c.u = (uint32_t)bf16_rne(f) << 16;
+            f = c.f;
+        }
+        dst[j] = (double)f;
+    }
+}
+
 /* Cache slab [n_bg][n_slots][head_dim] holding slots slot0..slot0+n_slots-1 of heads
  * bg0..bg0+n_bg-1: element index = ((bg * pitch) + slot) * head_dim + d. */
 void synth_fill_cache(void* dst, int dtype, uint64_t bg0, uint64_t n_bg, uint64_t slot0,

@@ -43,6 +43,8 @@ def cpu_lib():
         u64, dbl = ctypes.c_uint64, ctypes.c_double
         lib.synth_fill_flat.argtypes = [ctypes.c_void_p, ctypes.c_int, u64, u64, u64, u64, dbl, dbl]
         lib.synth_fill_flat.restype = None
+        lib.synth_fill_flat_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, u64, u64, u64, u64, dbl, dbl]
+        lib.synth_fill_flat_f64.restype = None
         lib.synth_fill_cache.argtypes = [ctypes.c_void_p, ctypes.c_int, u64, u64, u64, u64, u64, u64,
                                          u64, u64, dbl, dbl]
         lib.synth_fill_cache.restype = None
@@ -78,6 +80,13 @@ def _np_dtype(dtype: str):
 def cpu_fill_flat(n: int, start: int, seed: int, tid: int, mean: float, std: float, dtype: str) -> np.ndarray:
     out = np.empty(n, dtype=_np_dtype(dtype))
     cpu_lib().synth_fill_flat(out.ctypes.data, _dt(dtype), n, start, seed, tid, mean, gen.scale_for(std))
+    return out
+
+
+def cpu_fill_flat_f64(n: int, start: int, seed: int, tid: int, mean: float, std: float, dtype: str) -> np.ndarray:
+    """Stored values widened exactly to float64 (same as gen.to_f64 of cpu_fill_flat)."""
+    out = np.empty(n, dtype=np.float64)
+    cpu_lib().synth_fill_flat_f64(out.ctypes.data, _dt(dtype), n, start, seed, tid, mean, gen.scale_for(std))
     return out
 
 

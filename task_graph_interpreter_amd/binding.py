@@ -1,0 +1,239 @@
+"""Thin ctypes binding of libmk.so (declared in include/mk.h).
+
+Argument marshalling only: every step of the decode path runs in the library's HIP
+kernels.  Functions keep the C names; device memory and streams are passed as
+integer addresses (for example ``tensor.data_ptr()`` and
+``torch.cuda.current_stream().cuda_stream``).  Loading fails loudly if the library
+has not been built -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_ABI_VERSION = 1
+MK_OK, MK_ERR_ABI, MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6
+MK_STATUS_TIMEOUT, MK_STATUS_BAD_POSITION, MK_STATUS_BAD_TOKEN = 0x10000000, 0x20000000, 0x30000000
+MK_STATUS_KIND_MASK = 0xF0000000
+MK_DTYPE = {"f32": 0, "bf16": 1}
+
+# Every symbol include/mk.h declares.
+EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
+           "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
+           "mk_decode_step_per_op", "mk_status", "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid",
+           "mk_destroy", "mk_last_error", "mk_abi_version"]
+
+
+class MkTask(ctypes.Structure):
+    _fields_ = [("op_id", ctypes.c_uint16), ("config_id", ctypes.c_uint16), ("step", ctypes.c_uint16),
+                ("flags", ctypes.c_uint16), ("remaining_deps", ctypes.c_int32), ("num_dependents", ctypes.c_int32),
+                ("dependents_offset", ctypes.c_uint32), ("in_buf", ctypes.c_uint16 * 3),
+                ("out_buf", ctypes.c_uint16), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("kv_len", ctypes.c_int32), ("reserved", ctypes.c_uint32 * 5)]
+
+
+class MkModelCfg(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("struct_size", ctypes.c_uint32),
+                ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("batch", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("gemv_tiles", ctypes.c_int32), ("kv_chunk", ctypes.c_int32), ("join_nodes", ctypes.c_int32),
+                ("gemv_config", ctypes.c_int32), ("kv_capacity", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("kv_len", ctypes.POINTER(ctypes.c_int32))]
+
+
+class MkWeights(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_uint32), ("dev_ptrs", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class MkPlanInfo(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_uint32), ("n_edges", ctypes.c_uint32), ("n_buffers", ctypes.c_uint32),
+                ("n_levels", ctypes.c_uint32), ("scratch_bytes", ctypes.c_uint64),
+                ("kv_layer_bytes", ctypes.c_uint64)]
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mk error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
+    P = ctypes.POINTER
+    sig = {
+        "mk_plan": ([P(MkModelCfg), P(MkPlanInfo)], i32),
+        "mk_lower": ([P(MkModelCfg), P(vp)], i32),
+        "mk_lowered_tasks": ([vp, P(P(MkTask)), P(u32)], i32),
+        "mk_lowered_edges": ([vp, P(P(u32)), P(u32)], i32),
+        "mk_lowered_scratch_span": ([vp, u32, P(u64), P(u64)], i32),
+        "mk_lowered_free": ([vp], None),
+        "mk_build_graph": ([P(MkModelCfg), P(MkWeights), vp, vp, P(vp)], i32),
+        "mk_graph_tasks": ([vp, P(P(MkTask)), P(u32)], i32),
+        "mk_graph_edges": ([vp, P(P(u32)), P(u32)], i32),
+        "mk_decode_step": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "mk_decode_step_per_op": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "mk_status": ([vp, P(u32)], i32),
+        "mk_set_wait_limit": ([vp, u64], i32),
+        "mk_set_trace": ([vp, vp], i32),
+        "mk_graph_grid": ([vp, P(u32)], i32),
+        "mk_destroy": ([vp], None),
+        "mk_last_error": ([], ctypes.c_char_p),
+        "mk_abi_version": ([], u32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    if L.mk_abi_version() != MK_ABI_VERSION:
+        raise RuntimeError("libmk.so ABI version differs from the binding's")
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != MK_OK:
+        raise MkError(rc, lib().mk_last_error().decode())
+
+
+def mk_last_error() -> str:
+    return lib().mk_last_error().decode()
+
+
+def mk_abi_version() -> int:
+    return int(lib().mk_abi_version())
+
+
+def make_cfg(*, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, batch, rms_eps,
+             rope_theta, weight_dtype, kv_dtype, gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity,
+             kv_len):
+    """Build an mk_model_cfg; returns (cfg, keepalive) -- keep both alive during calls."""
+    kv = (ctypes.c_int32 * batch)(*[int(v) for v in kv_len])
+    c = MkModelCfg(MK_ABI_VERSION, ctypes.sizeof(MkModelCfg), n_layers, hidden, n_q_heads, n_kv_heads, head_dim,
+                   intermediate, vocab, batch, rms_eps, rope_theta, MK_DTYPE[weight_dtype], MK_DTYPE[kv_dtype],
+                   gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity, 0,
+                   ctypes.cast(kv, ctypes.POINTER(ctypes.c_int32)))
+    return c, kv
+
+
+def mk_plan(cfg: MkModelCfg) -> dict:
+    info = MkPlanInfo()
+    _check(lib().mk_plan(ctypes.byref(cfg), ctypes.byref(info)))
+    return {k: getattr(info, k) for k, _ in MkPlanInfo._fields_}
+
+
+def _tasks_to_numpy(ptr, n) -> np.ndarray:
+    raw = ctypes.string_at(ptr, n * 64) if n else b""
+    return np.frombuffer(raw, dtype=np.uint8).reshape(n, 64).copy()
+
+
+def _edges_to_numpy(ptr, n) -> np.ndarray:
+    if n == 0:
+        return np.zeros(0, dtype=np.uint32)
+    return np.ctypeslib.as_array(ptr, shape=(n,)).copy()
+
+
+class Lowered:
+    """Host-only lowering (mk_lower): raw descriptor bytes and edges, no GPU needed."""
+
+    def __init__(self, cfg: MkModelCfg):
+        h = ctypes.c_void_p()
+        _check(lib().mk_lower(ctypes.byref(cfg), ctypes.byref(h)))
+        self.h = h
+
+    def tasks_bytes(self) -> np.ndarray:
+        p, n = ctypes.POINTER(MkTask)(), ctypes.c_uint32()
+        _check(lib().mk_lowered_tasks(self.h, ctypes.byref(p), ctypes.byref(n)))
+        return _tasks_to_numpy(p, n.value)
+
+    def edges(self) -> np.ndarray:
+        p, n = ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_uint32()
+        _check(lib().mk_lowered_edges(self.h, ctypes.byref(p), ctypes.byref(n)))
+        return _edges_to_numpy(p, n.value)
+
+    def scratch_span(self, buf_index: int):
+        off, nb = ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().mk_lowered_scratch_span(self.h, buf_index, ctypes.byref(off), ctypes.byref(nb)))
+        return off.value, nb.value
+
+    def close(self):
+        if self.h:
+            lib().mk_lowered_free(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def mk_lower(cfg: MkModelCfg) -> Lowered:
+    return Lowered(cfg)
+
+
+class Graph:
+    """An uploaded graph (mk_build_graph); methods wrap the per-graph entry points."""
+
+    def __init__(self, cfg: MkModelCfg, weight_ptrs, scratch_ptr: int, stream: int):
+        arr = (ctypes.c_void_p * len(weight_ptrs))(*[int(p) for p in weight_ptrs])
+        w = MkWeights(len(weight_ptrs), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+        h = ctypes.c_void_p()
+        _check(lib().mk_build_graph(ctypes.byref(cfg), ctypes.byref(w), scratch_ptr, stream, ctypes.byref(h)))
+        self.h = h
+
+    def mk_decode_step(self, stream, tokens, positions, kcache, vcache, logits) -> None:
+        _check(lib().mk_decode_step(self.h, stream, tokens, positions, kcache, vcache, logits))
+
+    def mk_decode_step_per_op(self, stream, tokens, positions, kcache, vcache, logits) -> None:
+        _check(lib().mk_decode_step_per_op(self.h, stream, tokens, positions, kcache, vcache, logits))
+
+    def mk_status(self) -> int:
+        st = ctypes.c_uint32()
+        rc = lib().mk_status(self.h, ctypes.byref(st))
+        if rc not in (MK_OK, MK_ERR_DEVICE):
+            _check(rc)
+        return st.value
+
+    def mk_set_wait_limit(self, ticks: int) -> None:
+        _check(lib().mk_set_wait_limit(self.h, ticks))
+
+    def mk_set_trace(self, trace_ptr: int | None) -> None:
+        _check(lib().mk_set_trace(self.h, trace_ptr or None))
+
+    def mk_graph_grid(self) -> int:
+        n = ctypes.c_uint32()
+        _check(lib().mk_graph_grid(self.h, ctypes.byref(n)))
+        return n.value
+
+    def tasks_bytes(self) -> np.ndarray:
+        p, n = ctypes.POINTER(MkTask)(), ctypes.c_uint32()
+        _check(lib().mk_graph_tasks(self.h, ctypes.byref(p), ctypes.byref(n)))
+        return _tasks_to_numpy(p, n.value)
+
+    def edges(self) -> np.ndarray:
+        p, n = ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_uint32()
+        _check(lib().mk_graph_edges(self.h, ctypes.byref(p), ctypes.byref(n)))
+        return _edges_to_numpy(p, n.value)
+
+    def close(self) -> None:
+        if getattr(self, "h", None):
+            lib().mk_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def mk_build_graph(cfg, weight_ptrs, scratch_ptr, stream) -> Graph:
+    return Graph(cfg, weight_ptrs, scratch_ptr, stream)

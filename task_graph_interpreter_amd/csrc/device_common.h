@@ -1,0 +1,182 @@
+// Device-side shared pieces of the interpreter: launch arguments, buffer-table
+// resolution, bf16 conversion, wavefront reductions, and the readiness protocol
+// (acquire-wait on a task's own counter, release-increment of each dependent's).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mk.h"
+
+namespace mk {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 512;  // 8 wave64s per workgroup, one workgroup per CU
+constexpr int kWaves = kThreads / 64;
+// LDS: x staging / attention scores.  Above half of the CU's 160 KB, so the
+// persistent kernel gets exactly one workgroup per CU (co-residency of the grid).
+constexpr int kSmemBytes = 128 * 1024;
+constexpr int kRedFloats = 1024;  // reduction scratch
+
+// Buffer-table entry tags (top byte): 0 = absolute device pointer; otherwise an
+// offset into a per-step base passed at launch.
+enum : uint32_t { TAG_ABS = 0, TAG_KCACHE = 1, TAG_VCACHE = 2, TAG_TOKENS = 3, TAG_POSITIONS = 4, TAG_LOGITS = 5 };
+constexpr uint64_t kTagShift = 56;
+constexpr uint64_t kOffMask = (uint64_t(1) << kTagShift) - 1;
+
+struct Ctrl {
+  uint32_t head;    // ticket counter (monotone across steps)
+  uint32_t status;  // sticky device status word
+  uint32_t pad[62];
+};
+
+struct Smem {
+  float xs[kSmemBytes / 4];  // staged activations / scores
+  float red[kRedFloats];     // reductions
+  uint64_t t_ready;          // trace: when the dependency wait ended
+  uint32_t ticket;
+  uint32_t flag;
+};
+
+struct LaunchArgs {
+  const mk_task_t* tasks;
+  const uint32_t* edges;
+  const uint64_t* table;
+  uint32_t* arrivals;
+  Ctrl* ctrl;
+  uint64_t* trace;
+  uint64_t rt[8];  // per-step bases indexed by tag
+  uint32_t n_tasks;
+  uint32_t epoch;
+  uint32_t ticket_base;
+  uint32_t first_task;  // per-op launches: first task of the op
+  uint64_t wait_limit;  // ticks of the 100 MHz clock
+  float rms_eps, rope_theta;
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, batch, intermediate, vocab, kv_capacity;
+};
+
+__device__ __forceinline__ char* resolve(const LaunchArgs& a, uint32_t idx) {
+  const uint64_t e = a.table[idx];
+  const uint32_t tag = (uint32_t)(e >> kTagShift);
+  return (char*)(a.rt[tag] + (e & kOffMask));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum across groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Block-wide sum; every thread gets the result.  `red` needs kWaves floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+__device__ __forceinline__ uint64_t clock100() { return wall_clock64(); }
+
+__device__ __forceinline__ void raise_status(const LaunchArgs& a, uint32_t code) {
+  uint32_t expected = 0u;
+  __hip_atomic_compare_exchange_strong(&a.ctrl->status, &expected, code, __ATOMIC_RELAXED,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t read_status(const LaunchArgs& a) {
+  return __hip_atomic_load(&a.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until task t's counter shows all of this step's parents have arrived
+// (arrivals[t] - epoch * indeg >= 0 in wrapping 32-bit arithmetic), then acquire at
+// agent scope so every wave of the workgroup sees the producers' writes.  Bounded:
+// on timeout (or if another workgroup raised an error) the step is abandoned.
+// Returns false if the step was abandoned.  Called by all threads.
+__device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_t indeg, Smem& sm) {
+  if (indeg == 0) {
+    if (threadIdx.x == 0) sm.t_ready = clock100();
+    return true;
+  }
+  if (threadIdx.x == 0) {
+    const uint32_t target = a.epoch * (uint32_t)indeg;
+    uint32_t ok = 1;
+    uint32_t v = __hip_atomic_load(&a.arrivals[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - target) < 0) {
+      const uint64_t t0 = clock100();
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(&a.arrivals[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int32_t)(v - target) >= 0) break;
+        if (clock100() - t0 > a.wait_limit) {
+          raise_status(a, MK_STATUS_TIMEOUT | t);
+          ok = 0;
+          break;
+        }
+        if (read_status(a) != 0) {
+          ok = 0;
+          break;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sm.flag = ok;
+    sm.t_ready = clock100();
+  }
+  __syncthreads();
+  return sm.flag != 0;
+}
+
+// Make this workgroup's writes visible at agent scope, then count one arrival on
+// every dependent.  Called by all threads after the task body.
+__device__ __forceinline__ void release_dependents(const LaunchArgs& a, const mk_task_t& d) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t n = (uint32_t)d.num_dependents;
+    for (uint32_t i = threadIdx.x; i < n; i += 64) {
+      const uint32_t c = a.edges[d.dependents_offset + i];
+      __hip_atomic_fetch_add(&a.arrivals[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace mk

@@ -1,0 +1,360 @@
+// Runtime of the decode megakernel: the persistent interpreter kernel, the per-op
+// launch baseline built from the same task bodies, and the C ABI that uploads a
+// lowered graph and launches a step.
+//
+// Scheduling ("Megakernels", runhoid.com: "Megakernel iceberg" layer 6 and "Hoid's
+// approach to megakernels"): one workgroup per CU, all co-resident; each pulls the
+// next ticket of a device-wide counter, so tasks start in the lowering's topological
+// emission order ("Mega kernel initial", edge section); a task waits only for its own
+// readiness counter, and on completion increments the counter of every dependent
+// (the page's old queue path decremented remaining_deps; here the counters count
+// arrivals and never need resetting: task t is ready in step e once
+// arrivals[t] >= e * remaining_deps[t]).  Deadlock freedom: tickets are taken in
+// topological order and every workgroup is resident, so the lowest claimed but
+// unfinished task always has all of its parents finished.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+#include "tasks.h"
+
+namespace mk {
+
+template <bool TRACE>
+__global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) {
+  __shared__ Smem sm;
+  for (;;) {
+    uint64_t t_claim = 0;
+    if (threadIdx.x == 0) {
+      if (TRACE) t_claim = clock100();
+      uint32_t tk = __hip_atomic_fetch_add(&a.ctrl->head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                    a.ticket_base;
+      if (read_status(a) != 0) tk = 0xFFFFFFFFu;
+      sm.ticket = tk;
+    }
+    __syncthreads();
+    const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket);
+    if (t >= a.n_tasks) break;
+    const mk_task_t d = a.tasks[t];
+    run_task(a, d, t, sm);
+    uint64_t t_end = 0;
+    if (TRACE && threadIdx.x == 0) t_end = clock100();
+    release_dependents(a, d);
+    if (TRACE && threadIdx.x == 0) {
+      const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));  // XCC_ID
+      uint64_t* tr = a.trace + 4ull * t;
+      tr[0] = ((uint64_t)xcc << 32) | hw;
+      tr[1] = t_claim;
+      tr[2] = sm.t_ready;
+      tr[3] = t_end;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
+  __shared__ Smem sm;
+  const uint32_t t = a.first_task + blockIdx.x;
+  mk_task_t d = a.tasks[t];
+  d.remaining_deps = 0;  // stream order replaces the readiness counters
+  run_task(a, d, t, sm);
+}
+
+__global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) arrivals[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < sizeof(Ctrl) / 4) ((uint32_t*)ctrl)[threadIdx.x] = 0;
+}
+
+}  // namespace mk
+
+struct mk_graph {
+  mk::Lowered low;
+  int device = -1;
+  uint32_t grid = 0;
+  char* d_blob = nullptr;
+  mk_task_t* d_tasks = nullptr;
+  uint32_t* d_edges = nullptr;
+  uint64_t* d_table = nullptr;
+  uint32_t* d_arrivals = nullptr;
+  mk::Ctrl* d_ctrl = nullptr;
+  uint64_t* d_trace = nullptr;
+  uint32_t epoch = 0;
+  uint32_t ticket_base = 0;
+  uint64_t wait_limit = 200000000ull;
+  bool needs_reset = false;
+  hipStream_t last_stream = nullptr;
+};
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+  return mk::set_error(MK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                              \
+  do {                                             \
+    hipError_t e_ = (call);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) & (a - 1); }
+
+void free_graph(mk_graph* g) {
+  if (!g) return;
+  if (g->d_blob) (void)hipFree(g->d_blob);
+  if (g->d_table) (void)hipFree(g->d_table);
+  if (g->d_arrivals) (void)hipFree(g->d_arrivals);
+  if (g->d_ctrl) (void)hipFree(g->d_ctrl);
+  delete g;
+}
+
+mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t* positions, void* kcache,
+                         void* vcache, float* logits) {
+  mk::LaunchArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.tasks = g->d_tasks;
+  a.edges = g->d_edges;
+  a.table = g->d_table;
+  a.arrivals = g->d_arrivals;
+  a.ctrl = g->d_ctrl;
+  a.trace = g->d_trace;
+  a.rt[mk::TAG_ABS] = 0;
+  a.rt[mk::TAG_KCACHE] = (uint64_t)(uintptr_t)kcache;
+  a.rt[mk::TAG_VCACHE] = (uint64_t)(uintptr_t)vcache;
+  a.rt[mk::TAG_TOKENS] = (uint64_t)(uintptr_t)tokens;
+  a.rt[mk::TAG_POSITIONS] = (uint64_t)(uintptr_t)positions;
+  a.rt[mk::TAG_LOGITS] = (uint64_t)(uintptr_t)logits;
+  a.n_tasks = (uint32_t)g->low.tasks.size();
+  a.wait_limit = g->wait_limit;
+  const mk_model_cfg& c = g->low.cfg;
+  a.rms_eps = c.rms_eps;
+  a.rope_theta = c.rope_theta;
+  a.hidden = c.hidden;
+  a.n_q_heads = c.n_q_heads;
+  a.n_kv_heads = c.n_kv_heads;
+  a.head_dim = c.head_dim;
+  a.batch = c.batch;
+  a.intermediate = c.intermediate;
+  a.vocab = c.vocab;
+  a.kv_capacity = c.kv_capacity;
+  return a;
+}
+
+int check_step_args(mk_graph* g, const int32_t* tokens, const int32_t* positions, void* kcache, void* vcache,
+                    float* logits) {
+  if (!g) return mk::set_error(MK_ERR_INVALID, "graph is NULL");
+  if (!tokens || !positions || !kcache || !vcache || !logits)
+    return mk::set_error(MK_ERR_INVALID, "NULL device pointer");
+  if (misaligned(kcache, 16) || misaligned(vcache, 16) || misaligned(logits, 16) || misaligned(tokens, 4) ||
+      misaligned(positions, 4))
+    return mk::set_error(MK_ERR_ALIGN, "kcache/vcache/logits must be 16-byte aligned");
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != g->device) return mk::set_error(MK_ERR_INVALID, "current device differs from the graph's device");
+  return MK_OK;
+}
+
+int reset_state(mk_graph* g, hipStream_t s) {
+  const uint32_t n = (uint32_t)g->low.tasks.size();
+  const uint32_t blocks = (n + 255) / 256 > 0 ? (n + 255) / 256 : 1;
+  hipLaunchKernelGGL(mk::reset_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0, s, g->d_arrivals, n,
+                     g->d_ctrl);
+  HIP_TRY(hipGetLastError());
+  g->epoch = 0;
+  g->ticket_base = 0;
+  g->needs_reset = false;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scratch_dev, void* stream,
+                   mk_graph** out) {
+  if (!out) return mk::set_error(MK_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  mk_graph* g = new (std::nothrow) mk_graph();
+  if (!g) return mk::set_error(MK_ERR_NOMEM, "out of host memory");
+  int rc;
+  try {
+    rc = mk::lower(cfg, g->low);
+  } catch (const std::bad_alloc&) {
+    rc = mk::set_error(MK_ERR_NOMEM, "out of host memory while lowering");
+  }
+  if (rc) {
+    free_graph(g);
+    return rc;
+  }
+  const mk::Lowered& L = g->low;
+  const mk::BufIdx& bi = L.bi;
+  const int nl = L.cfg.n_layers;
+  auto fail = [&](int code) {
+    free_graph(g);
+    return code;
+  };
+  if (!weights || weights->count != 3u + 6u * nl || !weights->dev_ptrs)
+    return fail(mk::set_error(MK_ERR_INVALID, "weights: expected 3 + 6 * n_layers device pointers"));
+  for (uint32_t i = 0; i < weights->count; ++i) {
+    if (!weights->dev_ptrs[i]) return fail(mk::set_error(MK_ERR_INVALID, "weights: NULL pointer"));
+    if (misaligned(weights->dev_ptrs[i], 16)) return fail(mk::set_error(MK_ERR_ALIGN, "weights: pointer not 16-byte aligned"));
+  }
+  if (!scratch_dev) return fail(mk::set_error(MK_ERR_INVALID, "scratch_dev is NULL"));
+  if (misaligned(scratch_dev, 256)) return fail(mk::set_error(MK_ERR_ALIGN, "scratch_dev not 256-byte aligned"));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipGetDevice(&g->device);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipGetDevice"));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, g->device);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipGetDeviceProperties"));
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk::interpreter_kernel<false>, mk::kThreads, 0);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"));
+  if (per_cu < 1) return fail(mk::set_error(MK_ERR_INVALID, "interpreter kernel cannot be resident"));
+  g->grid = (uint32_t)prop.multiProcessorCount;  // one workgroup per CU
+
+  // Buffer table: absolute pointers for weights and scratch, tagged offsets for the
+  // per-step buffers (tokens, positions, caches, logits) resolved from launch args.
+  std::vector<uint64_t> table(bi.count(), 0);
+  auto W = [&](uint32_t i) { return (uint64_t)(uintptr_t)weights->dev_ptrs[i]; };
+  table[bi.tokens()] = (uint64_t)mk::TAG_TOKENS << mk::kTagShift;
+  table[bi.positions()] = (uint64_t)mk::TAG_POSITIONS << mk::kTagShift;
+  table[bi.embedding()] = W(0);
+  for (int l = 0; l < nl; ++l) {
+    table[bi.layer(l, mk::W_ATTN_NORM)] = W(1 + 6 * l + 0);
+    table[bi.layer(l, mk::W_QKV)] = W(1 + 6 * l + 1);
+    table[bi.layer(l, mk::W_O)] = W(1 + 6 * l + 2);
+    table[bi.layer(l, mk::W_MLP_NORM)] = W(1 + 6 * l + 3);
+    table[bi.layer(l, mk::W_GATE_UP)] = W(1 + 6 * l + 4);
+    table[bi.layer(l, mk::W_DOWN)] = W(1 + 6 * l + 5);
+    table[bi.layer(l, mk::KCACHE)] = ((uint64_t)mk::TAG_KCACHE << mk::kTagShift) | (uint64_t)l * L.kv_layer_bytes;
+    table[bi.layer(l, mk::VCACHE)] = ((uint64_t)mk::TAG_VCACHE << mk::kTagShift) | (uint64_t)l * L.kv_layer_bytes;
+  }
+  table[bi.final_norm()] = W(1 + 6 * nl);
+  table[bi.w_lm()] = W(2 + 6 * nl);
+  for (uint32_t i = 0; i < bi.count(); ++i)
+    if (L.scratch_off[i] != UINT64_MAX) table[i] = (uint64_t)(uintptr_t)scratch_dev + L.scratch_off[i];
+  table[bi.logits()] = (uint64_t)mk::TAG_LOGITS << mk::kTagShift;
+
+  // One blob: 64-byte header, task array, edge array.
+  const size_t nt = L.tasks.size(), ne = L.edges.size();
+  const size_t blob_bytes = sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t) + ne * sizeof(uint32_t);
+  std::vector<char> blob(blob_bytes);
+  std::memcpy(blob.data(), &L.header, sizeof(mk::BlobHeader));
+  std::memcpy(blob.data() + sizeof(mk::BlobHeader), L.tasks.data(), nt * sizeof(mk_task_t));
+  if (ne) std::memcpy(blob.data() + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t), L.edges.data(), ne * 4);
+  if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
+  if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
+  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(arrivals)"));
+  if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
+  g->d_tasks = (mk_task_t*)(g->d_blob + sizeof(mk::BlobHeader));
+  g->d_edges = (uint32_t*)(g->d_blob + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t));
+  if ((e = hipMemcpyAsync(g->d_blob, blob.data(), blob_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail(hip_fail(e, "hipMemcpyAsync(blob)"));
+  if ((e = hipMemcpyAsync(g->d_table, table.data(), table.size() * 8, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail(hip_fail(e, "hipMemcpyAsync(table)"));
+  if ((rc = reset_state(g, s)) != MK_OK) return fail(rc);
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail(hip_fail(e, "hipStreamSynchronize"));
+  g->last_stream = s;
+  *out = g;
+  return MK_OK;
+}
+
+int mk_graph_tasks(const mk_graph* g, const mk_task_t** tasks, uint32_t* n) {
+  if (!g || !tasks || !n) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  *tasks = g->low.tasks.data();
+  *n = (uint32_t)g->low.tasks.size();
+  return MK_OK;
+}
+
+int mk_graph_edges(const mk_graph* g, const uint32_t** edges, uint32_t* n) {
+  if (!g || !edges || !n) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  *edges = g->low.edges.data();
+  *n = (uint32_t)g->low.edges.size();
+  return MK_OK;
+}
+
+int mk_graph_grid(const mk_graph* g, uint32_t* workgroups) {
+  if (!g || !workgroups) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  *workgroups = g->grid;
+  return MK_OK;
+}
+
+int mk_set_wait_limit(mk_graph* g, uint64_t ticks) {
+  if (!g || ticks == 0) return mk::set_error(MK_ERR_INVALID, "graph is NULL or limit is 0");
+  g->wait_limit = ticks;
+  return MK_OK;
+}
+
+int mk_set_trace(mk_graph* g, uint64_t* trace_dev) {
+  if (!g) return mk::set_error(MK_ERR_INVALID, "graph is NULL");
+  if (misaligned(trace_dev, 8)) return mk::set_error(MK_ERR_ALIGN, "trace buffer not 8-byte aligned");
+  g->d_trace = trace_dev;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
+                   void* kcache_dev, void* vcache_dev, float* logits_dev) {
+  int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (g->needs_reset && (rc = reset_state(g, s)) != MK_OK) return rc;
+  mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  a.epoch = g->epoch + 1;
+  a.ticket_base = g->ticket_base;
+  void* params[] = {&a};
+  hipError_t e;
+  if (g->d_trace)
+    e = hipLaunchCooperativeKernel((const void*)mk::interpreter_kernel<true>, dim3(g->grid), dim3(mk::kThreads),
+                                   params, 0, s);
+  else
+    e = hipLaunchCooperativeKernel((const void*)mk::interpreter_kernel<false>, dim3(g->grid), dim3(mk::kThreads),
+                                   params, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(interpreter)");
+  g->epoch += 1;
+  g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
+  g->last_stream = s;
+  return MK_OK;
+}
+
+int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
+                          void* kcache_dev, void* vcache_dev, float* logits_dev) {
+  int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  for (const mk::OpRange& op : g->low.ops) {
+    a.first_task = op.first;
+    hipLaunchKernelGGL(mk::per_op_kernel, dim3(op.count), dim3(mk::kThreads), 0, s, a);
+  }
+  HIP_TRY(hipGetLastError());
+  g->last_stream = s;
+  return MK_OK;
+}
+
+int mk_status(mk_graph* g, uint32_t* device_status) {
+  if (!g || !device_status) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  HIP_TRY(hipStreamSynchronize(g->last_stream));
+  uint32_t st = 0;
+  HIP_TRY(hipMemcpy(&st, &g->d_ctrl->status, 4, hipMemcpyDeviceToHost));
+  *device_status = st;
+  if (st != 0) {
+    g->needs_reset = true;
+    char buf[96];
+    std::snprintf(buf, sizeof(buf), "device status 0x%08x (kind 0x%x, task %u)", st, st >> 28, st & 0x0FFFFFFFu);
+    return mk::set_error(MK_ERR_DEVICE, buf);
+  }
+  return MK_OK;
+}
+
+void mk_destroy(mk_graph* g) {
+  if (!g) return;
+  if (g->last_stream) (void)hipStreamSynchronize(g->last_stream);
+  free_graph(g);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""The C-ABI library: loads without a GPU, exports every declared symbol, validates
+configurations, and its host lowering equals the oracle lowering byte for byte."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import task_graph_interpreter_amd as mk
+from task_graph_interpreter_amd import binding
+from oracle import graph as og
+from synth import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mk.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(binding.LIB_PATH):
+        from task_graph_interpreter_amd import build
+        build.build()
+
+
+def test_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*|uint32_t)\s+(mk_\w+)\s*\(", text, re.M))
+    assert declared == set(binding.EXPORTS)
+    L = mk.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert mk.mk_abi_version() == binding.MK_ABI_VERSION
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(binding.MkTask) == 64
+    for name, off, size in [("op_id", 0, 2), ("remaining_deps", 8, 4), ("in_buf", 20, 6), ("out_buf", 26, 2),
+                            ("kv_len", 40, 4), ("reserved", 44, 20)]:
+        f = getattr(binding.MkTask, name)
+        assert f.offset == off and f.size == size
+    assert ctypes.sizeof(binding.MkModelCfg) == 88
+
+
+def _cfg(w, **over):
+    f = w.mk_fields()
+    f.update(over)
+    return mk.make_cfg(**f)
+
+
+def test_abi_mismatch_fails_loudly():
+    cfg, keep = _cfg(workloads.tiny())
+    cfg.struct_size = 80
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan(cfg)
+    assert e.value.code == binding.MK_ERR_ABI
+
+
+@pytest.mark.parametrize("over,msg", [
+    (dict(n_kv_heads=3), "n_q_heads"),
+    (dict(gemv_tiles=10_000), "gemv_tiles"),
+    (dict(kv_len=(129,)), "kv_len"),
+    (dict(gemv_config=1), "gemv_config"),
+    (dict(head_dim=63), "head_dim"),
+    (dict(kv_chunk=100_000), "kv_chunk"),
+])
+def test_invalid_configs_rejected(over, msg):
+    cfg, keep = _cfg(workloads.tiny(), **over)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan(cfg)
+    assert e.value.code == binding.MK_ERR_INVALID and msg in str(e.value)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+@pytest.mark.parametrize("joins", [1, 0])
+def test_cpp_lowering_equals_oracle_lowering(name, joins):
+    w = workloads.get(name).replace(join_nodes=joins)
+    cfg, keep = _cfg(w)
+    lo = mk.mk_lower(cfg)
+    tasks, edges = og.build_graph(w)
+    assert np.array_equal(lo.tasks_bytes(), tasks.view(np.uint8).reshape(-1, 64))
+    assert np.array_equal(lo.edges(), edges)
+    plan = mk.mk_plan(cfg)
+    assert plan["n_tasks"] == len(tasks) and plan["n_edges"] == len(edges)
+    assert plan["n_levels"] == int(og.levels(tasks, edges).max()) + 1
+
+
+def test_scratch_layout():
+    w = workloads.llama8b_ragged()
+    cfg, keep = _cfg(w)
+    lo = mk.mk_lower(cfg)
+    bi = og.BufferIndex(w)
+    spans = []
+    slots = sum(w.chunks(b) for b in range(w.batch)) * w.n_kv_heads
+    expect = {0: w.batch * w.qkv_cols, 1: w.batch * w.q_cols, 2: slots * w.grp * (w.head_dim + 2),
+              3: w.batch * w.q_cols, 4: w.batch * w.hidden, 5: w.batch * w.intermediate, 6: w.batch * w.hidden}
+    spans.append(lo.scratch_span(bi.x0))
+    for l in range(w.n_layers):
+        for j in range(7):
+            off, nb = lo.scratch_span(bi.act(l, j))
+            assert nb == 4 * expect[j]
+            spans.append((off, nb))
+    offs = [o for o, _ in spans]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert all(a[0] + a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    assert spans[-1][0] + spans[-1][1] <= mk.mk_plan(cfg)["scratch_bytes"]
+    with pytest.raises(mk.MkError):
+        lo.scratch_span(bi.w_lm)

@@ -30,6 +30,12 @@ def test_c_twin_bit_exact(dtype, mean, std):
     assert a.dtype == b.dtype and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def test_c_twin_f64_widening():
+    a = gen.to_f64(gen.fill(2, 4, 30000, 0.0, 0.02, "bf16", start=5), "bf16")
+    b = native.cpu_fill_flat_f64(30000, 5, 2, 4, 0.0, 0.02, "bf16")
+    assert np.array_equal(a, b)
+
+
 def test_c_twin_cache_layout():
     hd = 64
     a = native.cpu_fill_cache(3, 2, 5, 7, hd, 0, 9, 0.0, 1.0, "bf16")

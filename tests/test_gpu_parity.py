@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test builds a graph with mk_build_graph, runs mk_decode_step (the persistent
+interpreter) and/or mk_decode_step_per_op (one launch per op, same task bodies) and
+compares logits within |gpu - ref| <= 2e-2 + 1e-2 |ref|, greedy tokens exactly, and
+(on the small workloads) every activation buffer of the step.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode as od
+from oracle import graph as og
+from oracle.params import GeneratedParams
+from synth import gen, native, workloads
+from synth.device import DeviceInputs
+
+from gpu_common import MkRun, check_close, compare_activations
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    torch.cuda.init()
+
+
+def _oracle(w, keep=False, rows=None, split=False):
+    p = GeneratedParams(w)
+    return od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), rows=rows, keep=keep, split=split)
+
+
+def test_fill_kernel_matches_generator():
+    w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1)
+    _say("fill kernel vs numpy generator")
+    inp = DeviceInputs(w)
+    torch.cuda.synchronize()
+    for (tid, name, shape, mean, std, dtype), t in zip(w.weight_specs(), inp.weights):
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+        assert np.array_equal(got, gen.fill(w.seed, tid, got.size, mean, std, dtype)), name
+    kc = inp.kcache[1].view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = native.cpu_fill_cache(0, w.batch * w.n_kv_heads, 0, w.kv_capacity, w.head_dim, w.seed,
+                                w.tid_layer(1, workloads.KCACHE), 0.0, 1.0, "bf16")
+    assert np.array_equal(kc.reshape(ref.shape), ref)
+
+
+@pytest.mark.parametrize("path", ["persistent", "per_op"])
+def test_tiny_step_all_activations(path):
+    w = workloads.tiny()
+    _say(f"tiny one step, {path}")
+    run = MkRun(w)
+    logits = run.step(path)
+    ref, inter = _oracle(w, keep=True)
+    compare_activations(w, run.activations(), inter, range(w.batch))
+    check_close(logits, ref, "logits")
+    assert od.greedy_token(logits[0]) == od.greedy_token(ref[0])
+    run.close()
+
+
+def test_persistent_equals_per_op_bitwise_and_is_repeatable():
+    w = workloads.tiny()
+    _say("tiny persistent vs per-op bitwise, 5 repeats")
+    run = MkRun(w)
+    a = run.step("per_op")
+    for _ in range(5):
+        b = run.step("persistent")
+        assert np.array_equal(a, b)
+    run.close()
+
+
+@pytest.mark.parametrize("joins", [1, 0])
+def test_tiny_variants_bf16_batch_ragged(joins):
+    # bf16 weights and cache, 3 sequences of different lengths, GQA 8/2, tiles and
+    # chunks that do not divide the sizes evenly.
+    w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1, batch=3,
+                                 kv_len=(128, 41, 97), n_q_heads=8, gemv_tiles=5, kv_chunk=24,
+                                 join_nodes=joins, name="tiny_bf16_b3")
+    _say(f"tiny bf16 batch 3 ragged, joins={joins}")
+    run = MkRun(w)
+    logits = run.step("persistent")
+    ref, inter = _oracle(w, keep=True)
+    compare_activations(w, run.activations(), inter, range(w.batch))
+    check_close(logits, ref, "logits")
+    assert [od.greedy_token(r) for r in logits] == [od.greedy_token(r) for r in ref]
+    run.close()
+
+
+@pytest.mark.parametrize("path", ["persistent", "per_op"])
+def test_tiny_greedy_8_steps(path):
+    w = workloads.tiny().with_steps(8)
+    _say(f"tiny 8 greedy steps, {path}")
+    run = MkRun(w)
+    p = GeneratedParams(w)
+    kv = od.KVState(p)
+    tok = w.tokens()
+    pos = workloads.tiny().positions()
+    for s in range(8):
+        run.inp.set_step(tok, pos)
+        logits = run.step(path)
+        ref, _ = od.decode_step(w, p, tok, pos, kv)
+        check_close(logits, ref, f"logits step {s}")
+        t_gpu, t_ref = od.greedy_token(logits[0]), od.greedy_token(ref[0])
+        assert t_gpu == t_ref, (s, t_gpu, t_ref, od.top2_margin(ref[0]))
+        tok = np.array([t_ref], dtype=np.int32)
+        pos = pos + 1
+    run.close()
+
+
+def test_bad_position_reports_status_then_recovers():
+    w = workloads.tiny()
+    _say("tiny bad position status")
+    run = MkRun(w)
+    good = run.step("persistent")
+    run.inp.set_step(w.tokens(), np.array([w.kv_capacity], dtype=np.int32))
+    run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
+    st = run.graph.mk_status()
+    assert st & 0xF0000000 == 0x20000000
+    run.inp.set_step(w.tokens(), w.positions())
+    run.inp.refill_caches()
+    again = run.step("persistent")
+    assert np.array_equal(good, again)
+    run.close()
+
+
+def test_wait_timeout_drains_and_recovers():
+    # A 1-tick bound on every dependency wait: tasks whose producers are not done at
+    # the first look give up, the step drains, mk_status reports a timeout, and the
+    # next step with the normal bound is correct again.
+    w = workloads.tiny()
+    _say("tiny forced wait timeout")
+    run = MkRun(w)
+    good = run.step("persistent")
+    run.graph.mk_set_wait_limit(1)
+    run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
+    st = run.graph.mk_status()
+    assert st == 0 or st & 0xF0000000 == 0x10000000
+    run.graph.mk_set_wait_limit(200_000_000)
+    run.inp.refill_caches()
+    assert np.array_equal(run.step("persistent"), good)
+    run.close()
+
+
+def test_trace_mode_records_every_task():
+    w = workloads.tiny()
+    _say("tiny trace mode")
+    run = MkRun(w)
+    n = run.plan["n_tasks"]
+    trace = torch.zeros(n * 4, dtype=torch.int64, device="cuda")
+    run.graph.mk_set_trace(trace.data_ptr())
+    run.step("persistent")
+    run.graph.mk_set_trace(None)
+    tr = trace.cpu().numpy().reshape(n, 4)
+    assert (tr[:, 1] > 0).all()
+    assert (tr[:, 1] <= tr[:, 2]).all() and (tr[:, 2] <= tr[:, 3]).all()
+    tasks, edges = og.build_graph(w)
+    par = og.parents_from_csr(tasks, edges)
+    for t in range(n):  # a task becomes ready only after every parent ended
+        for p in par[t]:
+            assert tr[p, 3] <= tr[t, 2] + 1, (p, t)
+    run.close()
+
+
+def _big_parity(name, rows=None, steps=1):
+    w = workloads.get(name)
+    if steps > 1:
+        w = w.with_steps(steps)
+    _say(f"{name} parity, rows={rows}, steps={steps}")
+    run = MkRun(w)
+    p = GeneratedParams(w, backend="c")
+    kv = od.KVState(p)
+    tok = w.tokens()
+    pos = workloads.get(name).positions()
+    rows = list(range(w.batch)) if rows is None else rows
+    for s in range(steps):
+        run.inp.set_step(tok, pos)
+        logits = run.step("persistent")
+        ref, _ = od.decode_step(w, p, tok, pos, kv, rows=rows)
+        err = check_close(logits[rows], ref, f"{name} logits step {s}")
+        t_gpu = [od.greedy_token(logits[r]) for r in rows]
+        t_ref = [od.greedy_token(r) for r in ref]
+        assert t_gpu == t_ref, (s, t_gpu, t_ref, [od.top2_margin(r) for r in ref])
+        _say(f"{name} step {s}: max|dlogit|={err:.2e} tokens={t_ref}")
+        tok = np.array([od.greedy_token(logits[b]) for b in range(w.batch)], dtype=np.int32)
+        pos = pos + 1
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
+def test_1b_greedy_4_steps():
+    _big_parity("1b_b1", steps=4)
+
+
+def test_8b_b1_step():
+    _big_parity("8b_b1")
+
+
+def test_8b_b8_ragged_step():
+    _big_parity("8b_b8_ragged")
+
+
+def test_8b_b32_32k_step_sampled_rows():
+    _big_parity("8b_b32_32k", rows=[0, 1, 17, 31])
