@@ -1,0 +1,221 @@
+"""Decode-step benchmark of the persistent megakernel on one GPU.
+
+One step = one mk_decode_step: the whole decode step of the workload (embedding
+gather, every layer's GEMV tiles, RoPE-append, split-KV attention partials and
+combines, and the lm_head with the fused final norm) in ONE persistent-kernel launch.
+Inputs (seeded synthetic weights and KV caches) are resident in HBM before timing.
+
+Prints ONE JSON line: decode tokens/s over the timed steps, step latency, the HBM
+roofline fraction of the step (algorithmic bytes = every weight byte read once + the
+KV bytes attended, divided by the step time and by 8 TB/s), the same step run as one
+launch per op (same task bodies), and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload 8b_b1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/sec and step latency at 1 GPU; % of HBM roofline per step"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_layers=(1, 2)):
+    """The oracle (float64 numpy) timed on this host on a bounded sample: the full step
+    with 1 and with 2 layers (same shapes, weights generated beforehand), extrapolated
+    linearly to the workload's layer count."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import decode as od
+    from oracle.params import GeneratedParams
+
+    class Pregenerated:
+        def __init__(self, p, tids):
+            self.p = p
+            self.m = {t: p.matrix(t) for t in tids}
+
+        def embedding_row(self, tok):
+            return self.p.embedding_row(tok)
+
+        def vector(self, tid):
+            return self.p.vector(tid)
+
+        def matrix(self, tid):
+            return self.m[tid]
+
+        def cache(self, *a):
+            return self.p.cache(*a)
+
+    times = {}
+    for nl in budget_layers:
+        ws = w.replace(n_layers=nl)
+        p = GeneratedParams(ws, backend="c")
+        mats = [s[0] for s in ws.weight_specs() if len(s[2]) == 2 and s[1] != "embedding"]
+        pre = Pregenerated(p, mats)
+        kv = od.KVState(pre)
+        # warm the cache generator too: time only the oracle's arithmetic
+        for l in range(nl):
+            for b in range(ws.batch):
+                for g in range(ws.n_kv_heads):
+                    for which in (0, 1):
+                        pre.p.cache(l, which, b, g, 1)
+        t0 = time.perf_counter()
+        od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
+        times[nl] = time.perf_counter() - t0
+        del pre, kv
+    per_layer = times[2] - times[1]
+    fixed = times[1] - per_layer
+    est = fixed + w.n_layers * per_layer
+    blas = [i.get("num_threads", 1) for i in threadpool_info()]
+    cores = max([1] + blas)
+    return {"value": w.batch / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"float64 numpy oracle, full step of the same shapes with 1 layer ({times[1]:.2f} s) and "
+                       f"2 layers ({times[2]:.2f} s), extrapolated to {w.n_layers} layers = {est:.2f} s/step"),
+            "seconds_per_step_estimate": est}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8b_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-op", action="store_true")
+    ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py runs on one GPU only: the decode megakernel has no multi-GPU path "
+                  f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import task_graph_interpreter_amd as mk
+    from oracle import graph as og
+    from synth import workloads
+    from synth.device import DeviceInputs
+
+    w = workloads.get(args.workload)
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
+    inp = DeviceInputs(w)
+    cfg, keep = mk.make_cfg(**w.mk_fields())
+    plan = mk.mk_plan(cfg)
+    n_closed, _ = og.closed_form_counts(w.replace(join_nodes=0))
+    scratch = torch.zeros(plan["scratch_bytes"], dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    g = mk.mk_build_graph(cfg, inp.weight_ptrs(), scratch.data_ptr(), stream)
+    tasks = g.tasks_bytes()
+    n_nop = int((tasks[:, :2].copy().view(np.uint16)[:, 0] == 0).sum())  # op_id NOP = 0
+    assert plan["n_tasks"] - n_nop == n_closed, "timed graph must hold every layer and the lm_head"
+    ptrs = inp.step_ptrs()
+    torch.cuda.synchronize()
+
+    # Both paths must agree before anything is timed.
+    g.mk_decode_step(stream, *ptrs)
+    assert g.mk_status() == 0
+    mega = inp.logits.clone()
+    if not args.no_per_op:
+        g.mk_decode_step_per_op(stream, *ptrs)
+        torch.cuda.synchronize()
+        per_op_logits = inp.logits.clone()
+        diff = (per_op_logits - mega).abs().max().item()
+        assert diff <= 2e-2, f"per-op and persistent logits differ by {diff}"
+    log(f"graph: {plan['n_tasks']} tasks, {plan['n_edges']} edges, {plan['n_levels']} levels, grid {g.mk_graph_grid()}")
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn(stream, *ptrs)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            fn(stream, *ptrs)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        total = ev[0].elapsed_time(ev[steps])
+        return total, per
+
+    total, per = timed(g.mk_decode_step, args.steps, args.warmup)
+    assert g.mk_status() == 0
+    ms = total / args.steps
+    tok_s = w.batch * args.steps / (total / 1e3)
+    bytes_step = w.bytes_per_step()
+    achieved = bytes_step / (ms / 1e3) / 1e9
+    log(f"persistent: {ms:.4f} ms/step, {tok_s:.1f} tok/s, {achieved:.0f} GB/s")
+
+    per_op = None
+    if not args.no_per_op:
+        t2, per2 = timed(g.mk_decode_step_per_op, args.steps, args.warmup)
+        ms2 = t2 / args.steps
+        per_op = {"ms_per_step": ms2, "value": w.batch * args.steps / (t2 / 1e3), "unit": "tokens/s",
+                  "launches_per_step": 2 + 7 * w.n_layers,
+                  "latency_ms_median": float(np.median(per2)),
+                  "speedup_of_persistent": ms2 / ms}
+        log(f"per-op baseline: {ms2:.4f} ms/step")
+
+    if args.trace_out:
+        tr = torch.zeros(plan["n_tasks"] * 8, dtype=torch.int64, device="cuda")
+        g.mk_set_trace(tr.data_ptr())
+        g.mk_decode_step(stream, *ptrs)
+        torch.cuda.synchronize()
+        g.mk_set_trace(None)
+        np.save(args.trace_out, tr.cpu().numpy().reshape(-1, 8))
+        np.save(args.trace_out.replace(".npy", "_tasks.npy"), tasks)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w)
+        cpu.pop("seconds_per_step_estimate", None)
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "hidden": w.hidden, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "intermediate": w.intermediate,
+                   "vocab": w.vocab, "batch": w.batch, "kv_len": list(w.kv_len)[:4], "weight_dtype": w.weight_dtype,
+                   "kv_dtype": w.kv_dtype, "gemv_tiles": w.gemv_tiles, "kv_chunk": w.kv_chunk,
+                   "tasks": plan["n_tasks"], "edges": plan["n_edges"]},
+        "latency_ms": {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+                       "p90": float(np.percentile(per, 90))},
+        "bytes_per_step": bytes_step,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "per_op_baseline": per_op,
+        "cpu_baseline": cpu,
+    }
+    g.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -196,11 +196,11 @@ int mk_status(mk_graph* g, uint32_t* device_status);
  * the kernel drains instead of hanging. */
 int mk_set_wait_limit(mk_graph* g, uint64_t ticks);
 
-/* Trace mode: when `trace_dev` is non-NULL (device pointer, n_tasks * 4 uint64), the
- * next mk_decode_step calls record per task {XCC_ID << 32 | HW_ID register, claim
- * time, ready time (dependency wait over), end time (body done)}, times in ticks of
- * the constant 100 MHz clock.  NULL turns it off.  The pointer must stay valid while
- * steps that use it run. */
+/* Trace mode: when `trace_dev` is non-NULL (device pointer, n_tasks * 8 uint64), the
+ * next mk_decode_step calls record per task {XCC_ID << 32 | HW_ID register, start
+ * time, ready time (dependency wait over), body end time, release end time, 0, 0, 0},
+ * times in ticks of the constant 100 MHz clock.  NULL turns it off.  The pointer must
+ * stay valid while steps that use it run. */
 int mk_set_trace(mk_graph* g, uint64_t* trace_dev);
 
 /* Number of workgroups the persistent kernel is launched with (one per CU). */

@@ -1,24 +1,52 @@
-"""Build libmk.so (host lowering + HIP runtime and kernels for gfx950) in-tree."""
+"""Build libmk.so in-tree: host lowering + runtime, and one object per kernel
+specialisation listed in csrc/specs.def (compiled in parallel), linked together."""
 from __future__ import annotations
 
 import os
+import re
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["lower.cpp", "runtime.hip"]
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    cmd = ["hipcc", *FLAGS, *extra_flags, *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def specs():
+    """(name, args) of every MK_SPEC line in specs.def."""
+    out = []
+    for line in open(os.path.join(CSRC, "specs.def")):
+        m = re.match(r"\s*MK_SPEC\((\w+),\s*([^)]*)\)", line)
+        if m:
+            out.append((m.group(1), ",".join(a.strip() for a in m.group(2).split(","))))
+    return out
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"libmk build failed:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    steps = [(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "lower.cpp"), "-o", os.path.join(OBJ, "lower.o")]),
+             (["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "runtime.hip"), "-o", os.path.join(OBJ, "runtime.o")])]
+    objs = [os.path.join(OBJ, "lower.o"), os.path.join(OBJ, "runtime.o")]
+    for name, args in specs():
+        o = os.path.join(OBJ, f"kern_{name}.o")
+        steps.append(["hipcc", *HIP_FLAGS, f"-DMK_SPEC_FN=ks_{name}", f"-DMK_SPEC_ARGS={args}", "-c",
+                      os.path.join(CSRC, "kern_spec.hip"), "-o", o])
+        objs.append(o)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), steps))
+    _run(["hipcc", *HIP_FLAGS, "-shared", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -1,6 +1,7 @@
 // Device-side shared pieces of the interpreter: launch arguments, buffer-table
-// resolution, bf16 conversion, wavefront reductions, and the readiness protocol
-// (acquire-wait on a task's own counter, release-increment of each dependent's).
+// resolution, explicit global-memory accessors, bf16 conversion, wavefront
+// reductions, and the readiness protocol (acquire-wait on a task's own counter,
+// release-increment of each dependent's).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,11 +12,13 @@
 namespace mk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;  // 8 wave64s per workgroup, one workgroup per CU
 constexpr int kWaves = kThreads / 64;
-// LDS: x staging / attention scores.  Above half of the CU's 160 KB, so the
-// persistent kernel gets exactly one workgroup per CU (co-residency of the grid).
+// LDS: x staging / attention merge.  Above half of the CU's 160 KB, so the persistent
+// kernel gets exactly one workgroup per CU (co-residency of the whole grid).
 constexpr int kSmemBytes = 128 * 1024;
 constexpr int kRedFloats = 1024;  // reduction scratch
 
@@ -32,10 +35,11 @@ struct Ctrl {
 };
 
 struct Smem {
-  float xs[kSmemBytes / 4];  // staged activations / scores
-  float red[kRedFloats];     // reductions
-  uint64_t t_ready;          // trace: when the dependency wait ended
-  uint32_t ticket;
+  float xs[kSmemBytes / 4];       // staged activations / attention merge
+  float red[kRedFloats];          // reductions
+  alignas(16) mk_task_t desc[2];  // current / next descriptor (double-buffered)
+  uint64_t t_ready;               // trace: when the dependency wait ended
+  uint32_t ticket[2];
   uint32_t flag;
 };
 
@@ -56,10 +60,40 @@ struct LaunchArgs {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, batch, intermediate, vocab, kv_capacity;
 };
 
+// Every buffer lives in device global memory.  Pointers come out of the buffer table
+// as generic pointers; these accessors cast them to the global address space so the
+// compiler emits global_load/global_store (counted by vmcnt only) instead of flat
+// accesses (which also count against lgkmcnt and force full waits).
+#define MK_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T ldg(const void* p, size_t i) {
+  return ((const MK_GLOBAL T*)p)[i];
+}
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const void* p, size_t i) {
+  return __builtin_nontemporal_load(((const MK_GLOBAL T*)p) + i);
+}
+template <typename T>
+__device__ __forceinline__ void stg(void* p, size_t i, T v) {
+  ((MK_GLOBAL T*)p)[i] = v;
+}
+
+// Wave index as a wave-uniform (scalar) value, so branches on it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
 __device__ __forceinline__ char* resolve(const LaunchArgs& a, uint32_t idx) {
-  const uint64_t e = a.table[idx];
+  const uint64_t e = ldg<uint64_t>(a.table, idx);
   const uint32_t tag = (uint32_t)(e >> kTagShift);
-  return (char*)(a.rt[tag] + (e & kOffMask));
+  // Compare chain instead of indexing a.rt with a run-time tag (an indexed kernel
+  // argument would be copied to private memory).
+  uint64_t base = 0;
+  base = tag == TAG_KCACHE ? a.rt[TAG_KCACHE] : base;
+  base = tag == TAG_VCACHE ? a.rt[TAG_VCACHE] : base;
+  base = tag == TAG_TOKENS ? a.rt[TAG_TOKENS] : base;
+  base = tag == TAG_POSITIONS ? a.rt[TAG_POSITIONS] : base;
+  base = tag == TAG_LOGITS ? a.rt[TAG_LOGITS] : base;
+  return (char*)(base + (e & kOffMask));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -82,47 +116,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Wavefront sum with DPP moves only (no LDS): row_shr 1/2/4/8 leaves each 16-lane
+// row's sum in its lane 15, row_bcast15 and row_bcast31 fold the four rows into lane
+// 63.  Only lane 63 holds the total.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true);
+  return v + __int_as_float(s);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Sum across groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
-// Block-wide sum; every thread gets the result.  `red` needs kWaves floats.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += red[i];
-  return s;
-}
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float s = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) s = fmaxf(s, red[i]);
-  return s;
-}
-
 __device__ __forceinline__ uint64_t clock100() { return wall_clock64(); }
 
 __device__ __forceinline__ void raise_status(const LaunchArgs& a, uint32_t code) {
   uint32_t expected = 0u;
-  __hip_atomic_compare_exchange_strong(&a.ctrl->status, &expected, code, __ATOMIC_RELAXED,
+  __hip_atomic_compare_exchange_strong((MK_GLOBAL uint32_t*)&a.ctrl->status, &expected, code, __ATOMIC_RELAXED,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint32_t read_status(const LaunchArgs& a) {
-  return __hip_atomic_load(&a.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((MK_GLOBAL uint32_t*)&a.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until task t's counter shows all of this step's parents have arrived
@@ -136,14 +163,15 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
     return true;
   }
   if (threadIdx.x == 0) {
+    MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + t;
     const uint32_t target = a.epoch * (uint32_t)indeg;
     uint32_t ok = 1;
-    uint32_t v = __hip_atomic_load(&a.arrivals[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int32_t)(v - target) < 0) {
       const uint64_t t0 = clock100();
       for (;;) {
         __builtin_amdgcn_s_sleep(1);
-        v = __hip_atomic_load(&a.arrivals[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((int32_t)(v - target) >= 0) break;
         if (clock100() - t0 > a.wait_limit) {
           raise_status(a, MK_STATUS_TIMEOUT | t);
@@ -169,12 +197,12 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
 __device__ __forceinline__ void release_dependents(const LaunchArgs& a, const mk_task_t& d) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x < 64) {
+  if (wave_id() == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t n = (uint32_t)d.num_dependents;
-    for (uint32_t i = threadIdx.x; i < n; i += 64) {
-      const uint32_t c = a.edges[d.dependents_offset + i];
-      __hip_atomic_fetch_add(&a.arrivals[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t i = lane_id(); i < n; i += 64) {
+      const uint32_t c = ldg<uint32_t>(a.edges, d.dependents_offset + i);
+      __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -1,0 +1,163 @@
+// The persistent interpreter kernel and the per-op-launch baseline kernel, both
+// specialised at compile time for one model shape (Spec): weight and cache dtypes,
+// batch block, and the kblock counts (16-byte-per-lane row blocks) of the two GEMV
+// inner dimensions a decoder uses (hidden and intermediate).  Each specialisation is
+// compiled in its own translation unit (kern_*.hip); any shape without one runs the
+// generic specialisation, whose GEMV streams one kblock at a time.
+//
+// Scheduling ("Megakernels", runhoid.com: "Megakernel iceberg" layer 6 and "Hoid's
+// approach to megakernels"): one workgroup per CU, all co-resident; each pulls the
+// next ticket of a device-wide counter, so tasks start in the lowering's topological
+// emission order ("Mega kernel initial", edge section); a task waits only for its own
+// readiness counter, and on completion increments the counter of every dependent
+// (the page's old queue path decremented remaining_deps; here the counters count
+// arrivals and never need resetting: task t is ready in step e once
+// arrivals[t] >= e * remaining_deps[t]).  Deadlock freedom: tickets are taken in
+// topological order and every workgroup is resident, so the lowest claimed but
+// unfinished task always has all of its parents finished.
+#pragma once
+
+#include "tasks.h"
+
+namespace mk {
+
+template <bool WBF16_, bool KVBF16_, int BM_, int KBA_, int KBD_>
+struct Spec {
+  static constexpr bool WBF16 = WBF16_;    // weights bf16 (else fp32)
+  static constexpr bool KVBF16 = KVBF16_;  // KV cache bf16 (else fp32)
+  static constexpr int BM = BM_;           // batch rows per GEMV pass (1 or 8)
+  static constexpr int KBA = KBA_;         // kblocks of K = hidden (0: generic)
+  static constexpr int KBD = KBD_;         // kblocks of K = intermediate (0: generic)
+};
+
+// A row of KB kblocks -> (kblocks per segment, segments, rows in flight): 8 or 14
+// loads of 16 bytes in flight per lane.
+template <int BM, bool BF16, int KB>
+__device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm);
+  else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm);
+  else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm);
+  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm);
+  else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm);
+  else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm);
+  else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm);
+  else gemv_run<BM, BF16, 0, 1, 1>(a, d, t, sm);
+}
+
+template <class S>
+__device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  constexpr int VEC = S::WBF16 ? 8 : 4;
+  const int kb = (d.k / VEC + 63) >> 6;
+  if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm);
+  else if (S::KBD > 0 && S::KBD != S::KBA && kb == S::KBD) gemv_kb<S::BM, S::WBF16, S::KBD>(a, d, t, sm);
+  else gemv_run<S::BM, S::WBF16, 0, 1, 1>(a, d, t, sm);
+}
+
+template <class S>
+__device__ __forceinline__ void run_task_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  switch (d.op_id) {
+    case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm); break;
+    case MK_OP_ATTENTION_APPEND: task_append(a, d, t, sm); break;
+    case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16>(a, d, t, sm); break;
+    case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
+    case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
+    default: dep_wait(a, t, d.remaining_deps, sm); break;  // NOP join
+  }
+}
+
+__device__ __forceinline__ uint32_t claim_ticket(const LaunchArgs& a) {
+  return __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)&a.ctrl->head, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) - a.ticket_base;
+}
+
+// Thread 0 stages descriptor t (64 bytes) into LDS slot `slot`.
+__device__ __forceinline__ void stage_desc(const LaunchArgs& a, uint32_t t, Smem& sm, int slot) {
+  u32x4* dst = (u32x4*)&sm.desc[slot];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = ldg<u32x4>(a.tasks, (size_t)t * 4 + i);
+}
+
+// Every thread reads the staged descriptor as wave-uniform (scalar) values.
+__device__ __forceinline__ mk_task_t read_desc(const Smem& sm, int slot) {
+  uint32_t w[16];
+  const uint32_t* p = (const uint32_t*)&sm.desc[slot];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = __builtin_amdgcn_readfirstlane(p[i]);
+  mk_task_t d;
+  __builtin_memcpy(&d, w, sizeof(d));
+  return d;
+}
+
+// The persistent interpreter.  Tickets are claimed one task ahead (the claim's round
+// trip and the next descriptor's fetch overlap the current task); descriptors and
+// tickets are double-buffered in LDS, which is safe because every iteration ends in a
+// workgroup barrier.  Each workgroup makes exactly one failing claim per step, so the
+// ticket counter advances by n_tasks + grid per step and never needs a reset.
+// Trace mode (a.trace != null) records per-task timestamps.
+template <class S>
+__global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) {
+  __shared__ Smem sm;
+  const bool trace = a.trace != nullptr;
+  if (threadIdx.x == 0) {
+    uint32_t t0 = claim_ticket(a);
+    if (read_status(a) != 0) t0 = 0xFFFFFFFFu;
+    sm.ticket[0] = t0;
+    if (t0 < a.n_tasks) stage_desc(a, t0, sm, 0);
+  }
+  __syncthreads();
+  for (int it = 0;; it ^= 1) {
+    const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket[it]);
+    if (t >= a.n_tasks) break;
+    const mk_task_t d = read_desc(sm, it);
+    uint64_t t_claim = 0;
+    uint32_t nt = 0;
+    if (threadIdx.x == 0) {
+      if (trace) t_claim = clock100();
+      nt = claim_ticket(a);
+    }
+    run_task_spec<S>(a, d, t, sm);
+    uint64_t t_end = 0;
+    if (threadIdx.x == 0) {
+      if (trace) t_end = clock100();
+      if (read_status(a) != 0) nt = 0xFFFFFFFFu;
+      sm.ticket[it ^ 1] = nt;
+      if (nt < a.n_tasks) stage_desc(a, nt, sm, it ^ 1);
+    }
+    release_dependents(a, d);
+    if (trace && threadIdx.x == 0) {
+      const uint64_t t_rel = clock100();
+      const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));  // XCC_ID
+      stg<uint64_t>(a.trace, 8ull * t + 0, ((uint64_t)xcc << 32) | hw);
+      stg<uint64_t>(a.trace, 8ull * t + 1, t_claim);
+      stg<uint64_t>(a.trace, 8ull * t + 2, sm.t_ready);
+      stg<uint64_t>(a.trace, 8ull * t + 3, t_end);
+      stg<uint64_t>(a.trace, 8ull * t + 4, t_rel);
+    }
+  }
+}
+
+// One launch per op: blockIdx.x = task within the op; stream order replaces the
+// readiness counters.
+template <class S>
+__global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
+  __shared__ Smem sm;
+  const uint32_t t = a.first_task + blockIdx.x;
+  if (threadIdx.x == 0) stage_desc(a, t, sm, 0);
+  __syncthreads();
+  mk_task_t d = read_desc(sm, 0);
+  d.remaining_deps = 0;
+  run_task_spec<S>(a, d, t, sm);
+}
+
+struct KernelSet {
+  const void* persistent;
+  const void* per_op;
+};
+
+template <class S>
+KernelSet kernel_set() {
+  return KernelSet{(const void*)interpreter_kernel<S>, (const void*)per_op_kernel<S>};
+}
+
+}  // namespace mk

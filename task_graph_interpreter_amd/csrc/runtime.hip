@@ -1,17 +1,7 @@
-// Runtime of the decode megakernel: the persistent interpreter kernel, the per-op
-// launch baseline built from the same task bodies, and the C ABI that uploads a
-// lowered graph and launches a step.
-//
-// Scheduling ("Megakernels", runhoid.com: "Megakernel iceberg" layer 6 and "Hoid's
-// approach to megakernels"): one workgroup per CU, all co-resident; each pulls the
-// next ticket of a device-wide counter, so tasks start in the lowering's topological
-// emission order ("Mega kernel initial", edge section); a task waits only for its own
-// readiness counter, and on completion increments the counter of every dependent
-// (the page's old queue path decremented remaining_deps; here the counters count
-// arrivals and never need resetting: task t is ready in step e once
-// arrivals[t] >= e * remaining_deps[t]).  Deadlock freedom: tickets are taken in
-// topological order and every workgroup is resident, so the lowest claimed but
-// unfinished task always has all of its parents finished.
+// Host runtime of the decode megakernel: uploads a lowered graph (descriptor blob,
+// buffer table, readiness counters), picks the kernel specialisation for the model's
+// shape, and launches a step -- as ONE persistent kernel (mk_decode_step) or as one
+// launch per op of the same task bodies (mk_decode_step_per_op, the baseline).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -19,49 +9,50 @@
 #include <new>
 #include <string>
 
+#include "device_common.h"
 #include "internal.h"
-#include "tasks.h"
 
 namespace mk {
 
-template <bool TRACE>
-__global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) {
-  __shared__ Smem sm;
-  for (;;) {
-    uint64_t t_claim = 0;
-    if (threadIdx.x == 0) {
-      if (TRACE) t_claim = clock100();
-      uint32_t tk = __hip_atomic_fetch_add(&a.ctrl->head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                    a.ticket_base;
-      if (read_status(a) != 0) tk = 0xFFFFFFFFu;
-      sm.ticket = tk;
-    }
-    __syncthreads();
-    const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket);
-    if (t >= a.n_tasks) break;
-    const mk_task_t d = a.tasks[t];
-    run_task(a, d, t, sm);
-    uint64_t t_end = 0;
-    if (TRACE && threadIdx.x == 0) t_end = clock100();
-    release_dependents(a, d);
-    if (TRACE && threadIdx.x == 0) {
-      const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID
-      const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));  // XCC_ID
-      uint64_t* tr = a.trace + 4ull * t;
-      tr[0] = ((uint64_t)xcc << 32) | hw;
-      tr[1] = t_claim;
-      tr[2] = sm.t_ready;
-      tr[3] = t_end;
-    }
-  }
-}
+struct KernelSet {
+  const void* persistent;
+  const void* per_op;
+};
 
-__global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
-  __shared__ Smem sm;
-  const uint32_t t = a.first_task + blockIdx.x;
-  mk_task_t d = a.tasks[t];
-  d.remaining_deps = 0;  // stream order replaces the readiness counters
-  run_task(a, d, t, sm);
+// Specialisations compiled from kern_spec.hip, one object each.
+#define MK_SPEC(name, wbf16, kvbf16, bm, kba, kbd) KernelSet ks_##name();
+#include "specs.def"
+#undef MK_SPEC
+
+struct SpecEntry {
+  const char* name;
+  bool wbf16, kvbf16;
+  int bm, kba, kbd;
+  KernelSet (*get)();
+};
+
+static const SpecEntry kSpecs[] = {
+#define MK_SPEC(name, wbf16, kvbf16, bm, kba, kbd) {#name, wbf16, kvbf16, bm, kba, kbd, &ks_##name},
+#include "specs.def"
+#undef MK_SPEC
+};
+
+// kblocks of one weight row: 64 lanes x 16 bytes per kblock.
+static int kblocks(int K, bool bf16) { return (K * (bf16 ? 2 : 4) / 16 + 63) / 64; }
+
+// The specialisation whose compile-time row shapes match the model, else the generic
+// one of the same dtypes and batch block.
+static const SpecEntry* select_spec(const mk_model_cfg& c) {
+  const bool wb = c.weight_dtype == MK_DTYPE_BF16, kb = c.kv_dtype == MK_DTYPE_BF16;
+  const int bm = c.batch == 1 ? 1 : 8;
+  const int ka = kblocks(c.hidden, wb), kd = kblocks(c.intermediate, wb);
+  const SpecEntry* generic = nullptr;
+  for (const SpecEntry& s : kSpecs) {
+    if (s.wbf16 != wb || s.kvbf16 != kb || s.bm != bm) continue;
+    if (s.kba == ka && s.kbd == kd) return &s;
+    if (s.kba == 0 && s.kbd == 0) generic = &s;
+  }
+  return generic;
 }
 
 __global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
@@ -73,6 +64,8 @@ __global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
 
 struct mk_graph {
   mk::Lowered low;
+  const mk::SpecEntry* spec = nullptr;
+  mk::KernelSet kernels{};
   int device = -1;
   uint32_t grid = 0;
   char* d_blob = nullptr;
@@ -95,10 +88,10 @@ int hip_fail(hipError_t e, const char* what) {
   return mk::set_error(MK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-#define HIP_TRY(call)                              \
-  do {                                             \
-    hipError_t e_ = (call);                        \
-    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+#define HIP_TRY(call)                                  \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);  \
   } while (0)
 
 bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) & (a - 1); }
@@ -201,10 +194,14 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
     return fail(mk::set_error(MK_ERR_INVALID, "weights: expected 3 + 6 * n_layers device pointers"));
   for (uint32_t i = 0; i < weights->count; ++i) {
     if (!weights->dev_ptrs[i]) return fail(mk::set_error(MK_ERR_INVALID, "weights: NULL pointer"));
-    if (misaligned(weights->dev_ptrs[i], 16)) return fail(mk::set_error(MK_ERR_ALIGN, "weights: pointer not 16-byte aligned"));
+    if (misaligned(weights->dev_ptrs[i], 16))
+      return fail(mk::set_error(MK_ERR_ALIGN, "weights: pointer not 16-byte aligned"));
   }
   if (!scratch_dev) return fail(mk::set_error(MK_ERR_INVALID, "scratch_dev is NULL"));
   if (misaligned(scratch_dev, 256)) return fail(mk::set_error(MK_ERR_ALIGN, "scratch_dev not 256-byte aligned"));
+  g->spec = mk::select_spec(L.cfg);
+  if (!g->spec) return fail(mk::set_error(MK_ERR_INVALID, "no kernel specialisation for these dtypes"));
+  g->kernels = g->spec->get();
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipGetDevice(&g->device);
   if (e != hipSuccess) return fail(hip_fail(e, "hipGetDevice"));
@@ -212,7 +209,7 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   e = hipGetDeviceProperties(&prop, g->device);
   if (e != hipSuccess) return fail(hip_fail(e, "hipGetDeviceProperties"));
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk::interpreter_kernel<false>, mk::kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g->kernels.persistent, mk::kThreads, 0);
   if (e != hipSuccess) return fail(hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"));
   if (per_cu < 1) return fail(mk::set_error(MK_ERR_INVALID, "interpreter kernel cannot be resident"));
   g->grid = (uint32_t)prop.multiProcessorCount;  // one workgroup per CU
@@ -249,7 +246,8 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   if (ne) std::memcpy(blob.data() + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t), L.edges.data(), ne * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
   if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
-  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(arrivals)"));
+  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4)) != hipSuccess)
+    return fail(hip_fail(e, "hipMalloc(arrivals)"));
   if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
   g->d_tasks = (mk_task_t*)(g->d_blob + sizeof(mk::BlobHeader));
   g->d_edges = (uint32_t*)(g->d_blob + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t));
@@ -284,6 +282,8 @@ int mk_graph_grid(const mk_graph* g, uint32_t* workgroups) {
   return MK_OK;
 }
 
+const char* mk_graph_kernel_name(const mk_graph* g) { return g && g->spec ? g->spec->name : ""; }
+
 int mk_set_wait_limit(mk_graph* g, uint64_t ticks) {
   if (!g || ticks == 0) return mk::set_error(MK_ERR_INVALID, "graph is NULL or limit is 0");
   g->wait_limit = ticks;
@@ -307,13 +307,9 @@ int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const i
   a.epoch = g->epoch + 1;
   a.ticket_base = g->ticket_base;
   void* params[] = {&a};
-  hipError_t e;
-  if (g->d_trace)
-    e = hipLaunchCooperativeKernel((const void*)mk::interpreter_kernel<true>, dim3(g->grid), dim3(mk::kThreads),
-                                   params, 0, s);
-  else
-    e = hipLaunchCooperativeKernel((const void*)mk::interpreter_kernel<false>, dim3(g->grid), dim3(mk::kThreads),
-                                   params, 0, s);
+  // Cooperative launch: the runtime refuses the launch (instead of letting the
+  // spinning workgroups deadlock) if the whole grid cannot be resident at once.
+  hipError_t e = hipLaunchCooperativeKernel(g->kernels.persistent, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
   if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(interpreter)");
   g->epoch += 1;
   g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
@@ -327,11 +323,12 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev, 
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  a.trace = nullptr;
   for (const mk::OpRange& op : g->low.ops) {
     a.first_task = op.first;
-    hipLaunchKernelGGL(mk::per_op_kernel, dim3(op.count), dim3(mk::kThreads), 0, s, a);
+    void* params[] = {&a};
+    HIP_TRY(hipLaunchKernel(g->kernels.per_op, dim3(op.count), dim3(mk::kThreads), params, 0, s));
   }
-  HIP_TRY(hipGetLastError());
   g->last_stream = s;
   return MK_OK;
 }

@@ -1,0 +1,320 @@
+// Attention task bodies: ATTENTION_APPEND, ATTENTION_PARTIAL, ATTENTION_COMBINE
+// ("Mega kernel initial", OpId table and lowering section: one partial per (sequence,
+// KV-head group, KV chunk) producing (m, l, o), then a log-sum-exp merge -- plain
+// flash-decoding).
+#pragma once
+
+#include "device_common.h"
+
+namespace mk {
+
+// ---------------------------------------------------------------------------------
+// ATTENTION_APPEND ("RoPE-append current k,v"): for sequence b and KV head g, rotate
+// the group's query heads and k_g (rotate-half RoPE, angle pos * theta^(-2i/hd) with
+// the angle and its sine/cosine evaluated in fp64), write rotated q to q_rot and the
+// rotated k and v into cache slot positions[b], rounded to the cache dtype.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void rope_cs(int pos, int i, int hd, float theta, float& c, float& s) {
+  const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
+  const double ang = (double)pos * inv;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+__device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc = (int)d.reserved[2];
+  const int g = d.k, hd = d.n, cap = d.kv_len;
+  const int Hq = a.n_q_heads, Hkv = a.n_kv_heads;
+  const float* qkv = (const float*)resolve(a, d.in_buf[0]);
+  float* qrot = (float*)resolve(a, d.out_buf);
+  char* kc = resolve(a, d.reserved[3]);
+  char* vc = resolve(a, d.reserved[4]);
+  // positions is a per-step input (no producer task): read it before waiting.
+  const int pos = ldg<int32_t>((const void*)a.rt[TAG_POSITIONS], b);
+  // Rotation coefficients do not depend on producers either.
+  const int half = hd / 2;
+  const int nrot = (hc + 1) * half;
+  float cs_c = 0.f, cs_s = 0.f;
+  const int e0 = threadIdx.x;
+  if (e0 < nrot) rope_cs(pos, e0 % half, hd, a.rope_theta, cs_c, cs_s);
+  if (!dep_wait(a, t, d.remaining_deps, sm)) return;
+  if (pos < 0 || pos >= cap) {
+    if (threadIdx.x == 0) raise_status(a, MK_STATUS_BAD_POSITION | t);
+    return;
+  }
+  const size_t row = (size_t)b * (Hq + 2 * Hkv) * hd;
+  const size_t slot = (((size_t)b * Hkv + g) * cap + pos) * hd;
+  const bool bf16 = d.config_id == MK_DTYPE_BF16;
+  // (hc q heads + 1 k head) x half rotation pairs, then hd v elements.
+  for (int e = threadIdx.x; e < nrot + hd; e += kThreads) {
+    if (e < nrot) {
+      const int hh = e / half, i = e % half;
+      float c = cs_c, s = cs_s;
+      if (e != e0) rope_cs(pos, i, hd, a.rope_theta, c, s);
+      const size_t src = hh < hc ? row + (size_t)(h0 + hh) * hd : row + (size_t)(Hq + g) * hd;
+      const float x0 = ldg<float>(qkv, src + i), x1 = ldg<float>(qkv, src + i + half);
+      const float r0 = x0 * c - x1 * s;
+      const float r1 = x1 * c + x0 * s;
+      if (hh < hc) {
+        const size_t dst = (size_t)b * Hq * hd + (size_t)(h0 + hh) * hd;
+        stg<float>(qrot, dst + i, r0);
+        stg<float>(qrot, dst + i + half, r1);
+      } else if (bf16) {
+        stg<uint16_t>(kc, slot + i, f32_to_bf16_rne(r0));
+        stg<uint16_t>(kc, slot + i + half, f32_to_bf16_rne(r1));
+      } else {
+        stg<float>(kc, slot + i, r0);
+        stg<float>(kc, slot + i + half, r1);
+      }
+    } else {
+      const int i = e - nrot;
+      const float v = ldg<float>(qkv, row + (size_t)(Hq + Hkv + g) * hd + i);
+      if (bf16) stg<uint16_t>(vc, slot + i, f32_to_bf16_rne(v));
+      else stg<float>(vc, slot + i, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// ATTENTION_PARTIAL ("online-softmax over one KV chunk -> (m,l,o) scratch"): keys
+// [c*chunk, min((c+1)*chunk, positions[b]+1)) of KV head g, for the group's q heads.
+//   s_j = q.k_j / sqrt(hd); m = max s; l = sum e^(s-m); o = sum e^(s-m) v_j
+// (o unnormalised; an empty chunk gives (-inf, 0, 0)).  Slot layout [heads][hd + 2]:
+// o in [0, hd), m at hd, l at hd + 1.
+//
+// A key row is read by a group of hd*es/16 lanes (16 bytes each); the rows of the
+// chunk are spread over the workgroup in rounds.  Rows older than the new token are
+// static, so up to kPartRounds rounds of K and V are loaded before the dependency
+// wait; the new token's row (written by this step's APPEND) is read after it.  Each
+// lane group keeps a running (m, l, o) per head; groups are merged with the same
+// log-sum-exp rule across the wavefront (xor shuffles) and across wavefronts (LDS).
+// ---------------------------------------------------------------------------------
+constexpr int kPartRounds = 8;
+
+__device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2, float l2, const float* o2,
+                                          int n) {
+  const float M = fmaxf(m, m2);
+  const float a1 = (m == -INFINITY) ? 0.f : __expf(m - M);
+  const float a2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - M);
+  l = l * a1 + l2 * a2;
+  for (int e = 0; e < n; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  m = M;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
+  if (BF16) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w); f[4] = f[5] = f[6] = f[7] = 0.f;
+  }
+}
+
+// One pass over the chunk for query heads [hg, hg + HM) of the group; the first pass
+// (hg == 0) prefetches before waiting on the producers.
+template <bool BF16, int HM>
+__device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, int hg) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int VEC = 16 / ES;
+  constexpr int R = kPartRounds;
+  const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc_all = (int)d.reserved[2];
+  const int c = (int)d.reserved[3], base = (int)d.reserved[4];
+  const int g = d.k, hd = d.n, chunk = d.kv_len, nchunks = d.m;
+  const int cap = a.kv_capacity, Hkv = a.n_kv_heads, Hq = a.n_q_heads;
+  const int hc = (hc_all - hg) < HM ? (hc_all - hg) : HM;
+  const float* qrot = (const float*)resolve(a, d.in_buf[0]);
+  const int rowq = hd * ES / 16;  // 16-byte pieces per cache row
+  const size_t head_off = (((size_t)b * Hkv + g) * cap) * rowq;
+  const char* kc = resolve(a, d.in_buf[1]);
+  const char* vc = resolve(a, d.in_buf[2]);
+  const int stride = hd + 2;
+  float* out = (float*)resolve(a, d.out_buf);
+  const size_t out0 = ((size_t)(base + c) * hc_all + hg) * stride;
+  const int pos = ldg<int32_t>((const void*)a.rt[TAG_POSITIONS], b);
+  const bool bad = pos < 0 || pos >= cap || pos >= nchunks * chunk;
+  int hi = (c + 1) * chunk;
+  hi = hi < pos + 1 ? hi : pos + 1;
+  int lo = c * chunk;
+  lo = lo < hi ? lo : hi;
+  const int n = bad ? 0 : hi - lo;
+  const int jnew = pos - lo;  // row of the new token (if inside this chunk)
+
+  const int lane = lane_id(), wave = wave_id();
+  const int lpk = rowq, kpw = 64 / lpk, kpr = kWaves * kpw;
+  const int kl = lane / lpk, dl = lane % lpk;
+  const int jbase = wave * kpw + kl;  // this lane group's row in round 0
+  const int rounds = (n + kpr - 1) / kpr;
+  const bool first = hg == 0;
+  auto row_idx = [&](int j) { return head_off + (size_t)(lo + j) * rowq + dl; };
+
+  u32x4 kr[R], vr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = jbase + r * kpr;
+    if (r < rounds && j < n && (j != jnew || !first)) {
+      kr[r] = ldg<u32x4>(kc, row_idx(j));
+      vr[r] = ldg<u32x4>(vc, row_idx(j));
+    }
+  }
+  if (first) {
+    if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
+    if (bad) {
+      if (threadIdx.x == 0) raise_status(a, MK_STATUS_BAD_POSITION | t);
+      return false;
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)hd);
+  float q[HM][8];
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    if (h < hc) {
+      const size_t q4 = ((size_t)b * Hq * hd + (size_t)(h0 + hg + h) * hd + dl * VEC) / 4;
+      const f32x4 q0 = ldg<f32x4>(qrot, q4);
+      q[h][0] = q0.x * scale; q[h][1] = q0.y * scale; q[h][2] = q0.z * scale; q[h][3] = q0.w * scale;
+      if (VEC == 8) {
+        const f32x4 q1 = ldg<f32x4>(qrot, q4 + 1);
+        q[h][4] = q1.x * scale; q[h][5] = q1.y * scale; q[h][6] = q1.z * scale; q[h][7] = q1.w * scale;
+      } else {
+        q[h][4] = q[h][5] = q[h][6] = q[h][7] = 0.f;
+      }
+    }
+  }
+  float m[HM], l[HM], o[HM][8];
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+  for (int r0 = 0; r0 < rounds; r0 += R) {
+    if (r0 > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int j = jbase + (r0 + r) * kpr;
+        if (r0 + r < rounds && j < n) {
+          kr[r] = ldg<u32x4>(kc, row_idx(j));
+          vr[r] = ldg<u32x4>(vc, row_idx(j));
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r0 + r < rounds) {
+        const int j = jbase + (r0 + r) * kpr;
+        const bool ok = j < n;
+        u32x4 kv = kr[r], vv = vr[r];
+        if (first && r0 == 0 && ok && j == jnew) {  // new token's row, written by this step's APPEND
+          kv = ldg<u32x4>(kc, row_idx(j));
+          vv = ldg<u32x4>(vc, row_idx(j));
+        }
+        float kf[8], vf[8];
+        unpack<BF16>(kv, kf);
+        unpack<BF16>(vv, vf);
+#pragma unroll
+        for (int h = 0; h < HM; ++h) {
+          if (h < hc) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s = fmaf(kf[e], q[h][e], s);
+            s = group_sum(s, lpk);
+            if (ok) {
+              const float mn = fmaxf(m[h], s);
+              const float al = __expf(m[h] - mn);  // m = -inf -> 0
+              const float p = __expf(s - mn);
+              l[h] = fmaf(l[h], al, p);
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(o[h][e], al, p * vf[e]);
+              m[h] = mn;
+            }
+          }
+        }
+      }
+    }
+  }
+  // Merge the lane groups of the wavefront (offsets lpk .. 32).
+  for (int off = lpk; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      if (h < hc) {
+        const float m2 = __shfl_xor(m[h], off, 64), l2 = __shfl_xor(l[h], off, 64);
+        float o2[8];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(o[h][e], off, 64);
+        lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
+      }
+    }
+  }
+  // Merge the wavefronts through LDS: [wave][head][hd + 2].
+  float* part = sm.xs;
+  if (!first) __syncthreads();  // the previous pass may still read `part`
+  if (kl == 0) {
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      if (h < hc) {
+        float* pw = part + ((size_t)wave * HM + h) * stride;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) pw[dl * VEC + e] = o[h][e];
+        if (dl == 0) {
+          pw[hd] = m[h];
+          pw[hd + 1] = l[h];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < hc * stride; e += kThreads) {
+    const int h = e / stride, dd = e % stride;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, part[((size_t)w * HM + h) * stride + hd]);
+    float acc = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float* pw = part + ((size_t)w * HM + h) * stride;
+      const float al = (pw[hd] == -INFINITY) ? 0.f : __expf(pw[hd] - M);
+      if (dd < hd) acc = fmaf(pw[dd], al, acc);
+      else if (dd == hd + 1) acc = fmaf(pw[hd + 1], al, acc);
+    }
+    stg<float>(out, out0 + h * stride + dd, (dd == hd) ? M : acc);
+  }
+  return true;
+}
+
+template <bool KVBF16>
+__device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  const int hc = (int)d.reserved[2];
+  for (int hg = 0; hg < hc; hg += 4)
+    if (!partial_pass<KVBF16, 4>(a, d, t, sm, hg)) return;
+}
+
+// ---------------------------------------------------------------------------------
+// ATTENTION_COMBINE ("LSE-merge of the partials -> final O"): per head,
+// M = max_c m_c, w_c = e^(m_c - M), O = sum_c w_c o_c / sum_c w_c l_c.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc = (int)d.reserved[2];
+  const int base = (int)d.reserved[4], nch = d.m, hd = d.n;
+  const float* part = (const float*)resolve(a, d.in_buf[0]);
+  float* att = (float*)resolve(a, d.out_buf);
+  if (!dep_wait(a, t, d.remaining_deps, sm)) return;
+  const int Hq = a.n_q_heads;
+  for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
+    const int h = e / hd, dd = e % hd;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ldg<float>(part, ((size_t)(base + c) * hc + h) * (hd + 2) + hd));
+    float lam = 0.f, o = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const size_t s = ((size_t)(base + c) * hc + h) * (hd + 2);
+      const float m = ldg<float>(part, s + hd);
+      const float w = m == -INFINITY ? 0.f : __expf(m - M);
+      lam = fmaf(w, ldg<float>(part, s + hd + 1), lam);
+      o = fmaf(w, ldg<float>(part, s + dd), o);
+    }
+    stg<float>(att, (size_t)b * Hq * hd + (size_t)(h0 + h) * hd + dd, o / lam);
+  }
+}
+
+}  // namespace mk

@@ -1,0 +1,259 @@
+// GEMV task body ("Mega kernel initial", lowering section: one task per output-column
+// tile; descriptor section: flags SILU_MUL=1, ADD_RESIDUAL=2, RMS_NORM_INPUT=4):
+//   y[b, c] = sum_k xin[b, k] W[c, k]  (+ res[b, c] with ADD_RESIDUAL)
+//   xin = x (mean(x^2) + eps)^-1/2 gamma with RMS_NORM_INPUT; the scale r_b is applied
+//   to the finished dot product, the gamma product while staging x
+//   SILU_MUL: y[b, c] = silu(g) u with g from weight row c and u from row I + c.
+//
+// Streaming layout (HBM-bound; no MFMA: the contraction has M <= 8 rows):
+//  * wavefront w owns the tile's outputs w, w + 8, ...; each output is one logical
+//    weight row (two with SILU_MUL: gate, then up);
+//  * a row is read in "kblocks": 64 lanes x 16 contiguous bytes = 1 KB, coalesced;
+//  * one loop iteration consumes RPG whole rows held in a ring of RPG * KBT registers
+//    and refills each slot with the same kblock of the row RPG ahead, so RPG * KBT
+//    16-byte loads per lane stay in flight.  The loop body is straight-line code:
+//    loads are unconditional (rows past the wave's last one re-read that row; the
+//    results are discarded), so the compiler's wait counts stay exact instead of
+//    draining the ring at every branch;
+//  * the ring's first fill is issued before the dependency wait: weights are static,
+//    so the tile's first bytes arrive while its producers are still finishing;
+//  * the input rows are staged once per task in LDS (fp32, x * gamma);
+//  * a finished row is reduced across the wavefront with DPP (no LDS traffic) and
+//    parked in the register of lane (row % 64); parked results are stored 64 at a
+//    time, outside the streaming loop for every shape the workloads use.
+#pragma once
+
+#include "device_common.h"
+
+namespace mk {
+
+struct GemvGeom {
+  const char* W;
+  int K, KC;      // inner dim, 16-byte chunks per row
+  int c0, I;      // first output column, up-row offset (SILU_MUL)
+  int nout, NQ;   // outputs of this wave, logical rows of this wave
+  int wave;       // wave index (scalar)
+  int silu;
+};
+
+__device__ __forceinline__ u32x4 gemv_load(const GemvGeom& g, int q, int kb, int lane) {
+  q = q < g.NQ ? q : g.NQ - 1;  // past the last row: re-read it (discarded)
+  const int j = g.silu ? (q >> 1) : q;
+  const int row = g.c0 + g.wave + kWaves * j + ((g.silu && (q & 1)) ? g.I : 0);
+  int chunk = kb * 64 + lane;
+  chunk = chunk < g.KC ? chunk : g.KC - 1;  // partial last kblock: masked when consumed
+  // 32-bit byte offset from the (scalar) matrix base: every weight matrix is < 4 GiB
+  // (checked when lowering), so the load uses a scalar base + 32-bit vector offset.
+  const uint32_t off = ((uint32_t)row * (uint32_t)g.KC + (uint32_t)chunk) * 16u;
+  return __builtin_nontemporal_load((const MK_GLOBAL u32x4*)((const MK_GLOBAL char*)g.W + off));
+}
+
+template <int BM, bool BF16>
+__device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int K, int chunk, bool valid, int nb,
+                                             float acc[BM]) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  float wf[8];
+  if (BF16) {
+    wf[0] = bf16_lo(w.x); wf[1] = bf16_hi(w.x); wf[2] = bf16_lo(w.y); wf[3] = bf16_hi(w.y);
+    wf[4] = bf16_lo(w.z); wf[5] = bf16_hi(w.z); wf[6] = bf16_lo(w.w); wf[7] = bf16_hi(w.w);
+  } else {
+    wf[0] = __uint_as_float(w.x); wf[1] = __uint_as_float(w.y);
+    wf[2] = __uint_as_float(w.z); wf[3] = __uint_as_float(w.w);
+    wf[4] = wf[5] = wf[6] = wf[7] = 0.f;
+  }
+  const float m = valid ? 1.f : 0.f;  // a masked chunk contributes 0
+  chunk = valid ? chunk : 0;
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    if (b < nb) {
+      const f32x4* xb = (const f32x4*)(xs + b * K + chunk * VEC);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC / 4; ++e) {
+        const f32x4 xv = xb[e];
+        s = fmaf(wf[4 * e + 0], xv.x, s);
+        s = fmaf(wf[4 * e + 1], xv.y, s);
+        s = fmaf(wf[4 * e + 2], xv.z, s);
+        s = fmaf(wf[4 * e + 3], xv.w, s);
+      }
+      acc[b] = fmaf(s, m, acc[b]);
+    }
+  }
+}
+
+// Stage input rows b0 .. b0+nb-1 of x (x * gamma with RMS_NORM_INPUT) into LDS and
+// return r_b (1 without the norm) in rs[].
+template <int BM>
+__device__ __forceinline__ void gemv_stage(const float* x, const char* gamma, bool gamma_bf16, bool norm, int K,
+                                           int b0, int nb, float eps, Smem& sm, float rs[BM]) {
+  float ss[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b) ss[b] = 0.f;
+  const int K4 = K >> 2;
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    if (b < nb) {
+      f32x4* xo = (f32x4*)(sm.xs + b * K);
+      for (int k4 = threadIdx.x; k4 < K4; k4 += kThreads) {
+        f32x4 v = ldg<f32x4>(x, (size_t)(b0 + b) * K4 + k4);
+        if (norm) {
+          ss[b] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[b]))));
+          float g0, g1, g2, g3;
+          if (gamma_bf16) {
+            const u32x2 gv = ldg<u32x2>(gamma, k4);
+            g0 = bf16_lo(gv.x); g1 = bf16_hi(gv.x); g2 = bf16_lo(gv.y); g3 = bf16_hi(gv.y);
+          } else {
+            const f32x4 gv = ldg<f32x4>(gamma, k4);
+            g0 = gv.x; g1 = gv.y; g2 = gv.z; g3 = gv.w;
+          }
+          v.x *= g0; v.y *= g1; v.z *= g2; v.w *= g3;
+        }
+        xo[k4] = v;
+      }
+    }
+  }
+  if (norm) {
+    const int w = wave_id();
+#pragma unroll
+    for (int b = 0; b < BM; ++b) ss[b] = wave_sum(ss[b]);
+    if (lane_id() == 0) {
+#pragma unroll
+      for (int b = 0; b < BM; ++b) sm.red[w * BM + b] = ss[b];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      float s = 0.f;
+      for (int i = 0; i < kWaves; ++i) s += sm.red[i * BM + b];
+      rs[b] = 1.0f / sqrtf(s / (float)K + eps);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) rs[b] = 1.f;
+  }
+  __syncthreads();
+}
+
+// Store the parked results of logical rows [q_base, q_base + 64) of this wave (lane l
+// holds row q_base + l): SiLU*mul pairs gate (even row) with up (odd row) through a
+// lane swap; the residual is added at store time.
+template <int BM>
+__device__ __forceinline__ void gemv_flush(const GemvGeom& g, const float park[BM], int q_base, int nb, bool resid,
+                                           const float* res, float* y, int N, int b0) {
+  const int lane = lane_id();
+  const int q = q_base + lane;
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    if (b < nb) {
+      float v = park[b];
+      if (g.silu) {
+        const float up = __shfl_xor(v, 1, 64);
+        v = v / (1.f + __expf(-v)) * up;
+      }
+      const bool mine = q < g.NQ && (!g.silu || !(q & 1));
+      if (mine) {
+        const int j = g.silu ? (q >> 1) : q;
+        const int c = g.c0 + g.wave + kWaves * j;
+        const size_t o = (size_t)(b0 + b) * N + c;
+        stg<float>(y, o, v + (resid ? ldg<float>(res, o) : 0.f));
+      }
+    }
+  }
+}
+
+// A row is SEG segments of KBT kblocks (compile time; KBT = 0: any K, one kblock at a
+// time); RPG rows are in flight per wave.  Ring slot (r, kb) cycles through kblock
+// s * KBT + kb of row r for s = 0 .. SEG-1, then moves to the row RPG ahead.
+template <int BM, bool BF16, int KBT, int SEG, int RPG>
+__device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int KBS = KBT > 0 ? KBT : 1;
+  const int lane = lane_id();
+  GemvGeom g;
+  g.wave = wave_id();
+  g.W = resolve(a, d.in_buf[1]);
+  g.K = d.k;
+  g.KC = d.k / VEC;
+  g.c0 = (int)d.reserved[0];
+  g.I = (int)d.reserved[2];
+  g.silu = (d.flags & MK_FLAG_SILU_MUL) ? 1 : 0;
+  const int cnt = (int)d.reserved[1];
+  g.nout = cnt > g.wave ? (cnt - g.wave + kWaves - 1) / kWaves : 0;
+  g.NQ = g.nout << g.silu;
+  const int KB = KBT > 0 ? KBT : (g.KC + 63) >> 6;
+  const int N = d.n, B = d.m;
+  const float* x = (const float*)resolve(a, d.in_buf[0]);
+  const char* aux = d.in_buf[2] != 0xFFFF ? resolve(a, d.in_buf[2]) : nullptr;
+  float* y = (float*)resolve(a, d.out_buf);
+  const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
+  const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
+  int bp = (kSmemBytes / 4) / g.K;
+  bp = bp < BM ? bp : BM;
+  const int iters = (g.NQ + RPG - 1) / RPG;
+
+  for (int b0 = 0; b0 < B; b0 += bp) {
+    const int nb = (B - b0) < bp ? (B - b0) : bp;
+    u32x4 buf[RPG][KBS];
+    if (KBT > 0 && g.NQ > 0) {
+#pragma unroll
+      for (int r = 0; r < RPG; ++r)
+#pragma unroll
+        for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, r, kb, lane);
+    }
+    if (b0 == 0 && !dep_wait(a, t, d.remaining_deps, sm)) return;
+    float rs[BM];
+    gemv_stage<BM>(x, aux, d.config_id != MK_GEMV_F32, norm, g.K, b0, nb, a.rms_eps, sm, rs);
+    if (g.NQ > 0) {
+      float park[BM];
+#pragma unroll
+      for (int b = 0; b < BM; ++b) park[b] = 0.f;
+      for (int it = 0; it < iters; ++it) {
+        const int q0 = it * RPG;
+        // Short rows: the compiler may keep the staged input in registers across rows.
+        // Long rows: an opaque offset keeps the LDS reads inside the loop instead of
+        // pinning 8 registers per kblock.
+        int xoff = 0;
+        if (KBS * SEG > 8) asm volatile("" : "+v"(xoff));
+        const float* xsr = sm.xs + xoff;
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+          float acc[BM];
+#pragma unroll
+          for (int b = 0; b < BM; ++b) acc[b] = 0.f;
+          if (KBT > 0) {
+#pragma unroll
+            for (int s = 0; s < SEG; ++s) {
+#pragma unroll
+              for (int kb = 0; kb < KBS; ++kb) {
+                const int chunk = (s * KBS + kb) * 64 + lane;
+                gemv_consume<BM, BF16>(buf[r][kb], xsr, g.K, chunk, chunk < g.KC, nb, acc);
+                if (s + 1 < SEG) buf[r][kb] = gemv_load(g, q0 + r, (s + 1) * KBS + kb, lane);
+                else buf[r][kb] = gemv_load(g, q0 + RPG + r, kb, lane);
+              }
+            }
+          } else {
+            for (int kb = 0; kb < KB; ++kb) {
+              const int chunk = kb * 64 + lane;
+              const u32x4 w = gemv_load(g, q0 + r, kb, lane);
+              gemv_consume<BM, BF16>(w, sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
+            }
+          }
+          const int q = q0 + r;
+#pragma unroll
+          for (int b = 0; b < BM; ++b) {
+            if (b < nb) {
+              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(acc[b])), 63));
+              park[b] = (lane == (q & 63)) ? v * rs[b] : park[b];
+            }
+          }
+          if ((q & 63) == 63 && q + 1 < g.NQ)  // more than 64 rows per wave: flush now
+            gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
+        }
+      }
+      gemv_flush<BM>(g, park, ((g.NQ - 1) >> 6) << 6, nb, resid, (const float*)aux, y, N, b0);
+    }
+    if (b0 + bp < B) __syncthreads();  // LDS reused by the next batch block
+  }
+}
+
+}  // namespace mk

@@ -151,13 +151,13 @@ def test_trace_mode_records_every_task():
     _say("tiny trace mode")
     run = MkRun(w)
     n = run.plan["n_tasks"]
-    trace = torch.zeros(n * 4, dtype=torch.int64, device="cuda")
+    trace = torch.zeros(n * 8, dtype=torch.int64, device="cuda")
     run.graph.mk_set_trace(trace.data_ptr())
     run.step("persistent")
     run.graph.mk_set_trace(None)
-    tr = trace.cpu().numpy().reshape(n, 4)
+    tr = trace.cpu().numpy().reshape(n, 8)
     assert (tr[:, 1] > 0).all()
-    assert (tr[:, 1] <= tr[:, 2]).all() and (tr[:, 2] <= tr[:, 3]).all()
+    assert (tr[:, 1] <= tr[:, 2]).all() and (tr[:, 2] <= tr[:, 3]).all() and (tr[:, 3] <= tr[:, 4]).all()
     tasks, edges = og.build_graph(w)
     par = og.parents_from_csr(tasks, edges)
     for t in range(n):  # a task becomes ready only after every parent ended
