@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
     ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
+    ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
+                    help="how persistent workgroups find tasks: host-built lists or a ticket counter")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -122,6 +124,8 @@ def main():
     scratch = torch.zeros(plan["scratch_bytes"], dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     g = mk.mk_build_graph(cfg, inp.weight_ptrs(), scratch.data_ptr(), stream)
+    modes = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC}
+    g.mk_set_schedule(modes[args.schedule])
     tasks = g.tasks_bytes()
     n_nop = int((tasks[:, :2].copy().view(np.uint16)[:, 0] == 0).sum())  # op_id NOP = 0
     assert plan["n_tasks"] - n_nop == n_closed, "timed graph must hold every layer and the lm_head"
@@ -161,6 +165,14 @@ def main():
     bytes_step = w.bytes_per_step()
     achieved = bytes_step / (ms / 1e3) / 1e9
     log(f"persistent: {ms:.4f} ms/step, {tok_s:.1f} tok/s, {achieved:.0f} GB/s")
+
+    other = "dynamic" if args.schedule == "static" else "static"
+    g.mk_set_schedule(modes[other])
+    t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
+    assert g.mk_status() == 0
+    g.mk_set_schedule(modes[args.schedule])
+    alt = {"schedule": other, "ms_per_step": t_alt / args.steps}
+    log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
 
     per_op = None
     if not args.no_per_op:
@@ -204,13 +216,14 @@ def main():
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "intermediate": w.intermediate,
                    "vocab": w.vocab, "batch": w.batch, "kv_len": list(w.kv_len)[:4], "weight_dtype": w.weight_dtype,
                    "kv_dtype": w.kv_dtype, "gemv_tiles": w.gemv_tiles, "kv_chunk": w.kv_chunk,
-                   "tasks": plan["n_tasks"], "edges": plan["n_edges"]},
+                   "tasks": plan["n_tasks"], "edges": plan["n_edges"], "schedule": args.schedule},
         "latency_ms": {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
                        "p90": float(np.percentile(per, 90))},
         "bytes_per_step": bytes_step,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None},
         "per_op_baseline": per_op,
+        "other_schedule": alt,
         "cpu_baseline": cpu,
     }
     g.close()

@@ -157,6 +157,11 @@ int mk_lowered_edges(const mk_lowered* g, const uint32_t** edges, uint32_t* n);
 /* Byte offset and size of activation buffer `buf_index` inside the scratch block
  * (error for buffers that are not scratch). */
 int mk_lowered_scratch_span(const mk_lowered* g, uint32_t buf_index, uint64_t* offset, uint64_t* bytes);
+/* The static schedule mk_build_graph would compute for a grid of `workers`
+ * workgroups (see mk_set_schedule and mk_graph_schedule for the layout).  Arrays are
+ * owned by the mk_lowered object and replaced by the next call. */
+int mk_lowered_schedule(mk_lowered* g, uint32_t workers, const uint32_t** order,
+                        const uint32_t** offsets, double* est_us);
 void mk_lowered_free(mk_lowered* g);
 
 /* Lower, then upload descriptors + edges (one blob behind a 64-byte header) and the
@@ -205,6 +210,38 @@ int mk_set_trace(mk_graph* g, uint64_t* trace_dev);
 
 /* Number of workgroups the persistent kernel is launched with (one per CU). */
 int mk_graph_grid(const mk_graph* g, uint32_t* workgroups);
+
+/* Name of the kernel specialisation the graph runs (library-owned string; "" for a
+ * NULL graph). */
+const char* mk_graph_kernel_name(const mk_graph* g);
+
+/* How the persistent kernel's workgroups find their next task.
+ *
+ * MK_SCHED_STATIC (default): each workgroup walks its own list of task indices,
+ * computed once by mk_build_graph.  This follows the host-side grouping of task
+ * indices ahead of time in "Mega kernel initial" (1y33.com, the level section: task
+ * indices grouped, plus the offsets where each group starts), except that the groups
+ * are per workgroup, not per level, and no grid barrier separates them.  The lists
+ * come from simulating list scheduling in emission order with a byte-count cost
+ * model, which hands each workgroup one tile of every wide matmul and so removes
+ * the wave-quantisation tail of "Megakernels" (runhoid.com, Fig. 2).  Each list is in
+ * increasing task order.
+ * MK_SCHED_DYNAMIC: each workgroup claims the next task index from a device-wide
+ * ticket counter ("Megakernels", runhoid.com, Fig. 5 b: a queue the SMs pop from).
+ *
+ * In both modes NOP joins are never run as tasks: the parent whose arrival completes a
+ * NOP's count counts the arrivals on the NOP's dependents itself.  Takes effect from
+ * the next mk_decode_step; results are bitwise identical in both modes. */
+#define MK_SCHED_STATIC 0
+#define MK_SCHED_DYNAMIC 1
+int mk_set_schedule(mk_graph* g, int mode);
+
+/* The static schedule: `order` holds the non-NOP task indices grouped by workgroup,
+ * workgroup w's list is order[offsets[w] .. offsets[w + 1]), `workers` = grid size;
+ * `est_us` (may be NULL) receives the cost model's simulated step time.  Arrays are
+ * library-owned, valid until mk_destroy. */
+int mk_graph_schedule(const mk_graph* g, const uint32_t** order, const uint32_t** offsets,
+                      uint32_t* workers, double* est_us);
 
 void mk_destroy(mk_graph* g);
 const char* mk_last_error(void);

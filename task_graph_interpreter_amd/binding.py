@@ -20,13 +20,14 @@ MK_ABI_VERSION = 1
 MK_OK, MK_ERR_ABI, MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP, MK_ERR_NOMEM, MK_ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6
 MK_STATUS_TIMEOUT, MK_STATUS_BAD_POSITION, MK_STATUS_BAD_TOKEN = 0x10000000, 0x20000000, 0x30000000
 MK_STATUS_KIND_MASK = 0xF0000000
+MK_SCHED_STATIC, MK_SCHED_DYNAMIC = 0, 1
 MK_DTYPE = {"f32": 0, "bf16": 1}
 
 # Every symbol include/mk.h declares.
 EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
            "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
            "mk_decode_step_per_op", "mk_status", "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid",
-           "mk_destroy", "mk_last_error", "mk_abi_version"]
+           "mk_graph_kernel_name", "mk_set_schedule", "mk_graph_schedule", "mk_lowered_schedule", "mk_destroy", "mk_last_error", "mk_abi_version"]
 
 
 class MkTask(ctypes.Structure):
@@ -92,6 +93,10 @@ def lib():
         "mk_set_wait_limit": ([vp, u64], i32),
         "mk_set_trace": ([vp, vp], i32),
         "mk_graph_grid": ([vp, P(u32)], i32),
+        "mk_graph_kernel_name": ([vp], ctypes.c_char_p),
+        "mk_set_schedule": ([vp, i32], i32),
+        "mk_graph_schedule": ([vp, P(P(u32)), P(P(u32)), P(u32), P(ctypes.c_double)], i32),
+        "mk_lowered_schedule": ([vp, u32, P(P(u32)), P(P(u32)), P(ctypes.c_double)], i32),
         "mk_destroy": ([vp], None),
         "mk_last_error": ([], ctypes.c_char_p),
         "mk_abi_version": ([], u32),
@@ -142,6 +147,13 @@ def _tasks_to_numpy(ptr, n) -> np.ndarray:
     return np.frombuffer(raw, dtype=np.uint8).reshape(n, 64).copy()
 
 
+def _schedule_to_numpy(order_ptr, off_ptr, workers):
+    offsets = np.ctypeslib.as_array(off_ptr, shape=(workers + 1,)).copy()
+    n = int(offsets[-1])
+    order = np.ctypeslib.as_array(order_ptr, shape=(n,)).copy() if n else np.zeros(0, np.uint32)
+    return order, offsets
+
+
 def _edges_to_numpy(ptr, n) -> np.ndarray:
     if n == 0:
         return np.zeros(0, dtype=np.uint32)
@@ -165,6 +177,12 @@ class Lowered:
         p, n = ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_uint32()
         _check(lib().mk_lowered_edges(self.h, ctypes.byref(p), ctypes.byref(n)))
         return _edges_to_numpy(p, n.value)
+
+    def schedule(self, workers: int):
+        """Static schedule for `workers` workgroups: ((order, offsets), est_us)."""
+        o, f, est = ctypes.POINTER(ctypes.c_uint32)(), ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_double()
+        _check(lib().mk_lowered_schedule(self.h, workers, ctypes.byref(o), ctypes.byref(f), ctypes.byref(est)))
+        return _schedule_to_numpy(o, f, workers), est.value
 
     def scratch_span(self, buf_index: int):
         off, nb = ctypes.c_uint64(), ctypes.c_uint64()
@@ -216,6 +234,20 @@ class Graph:
         n = ctypes.c_uint32()
         _check(lib().mk_graph_grid(self.h, ctypes.byref(n)))
         return n.value
+
+    def mk_graph_kernel_name(self) -> str:
+        return lib().mk_graph_kernel_name(self.h).decode()
+
+    def mk_set_schedule(self, mode: int) -> None:
+        _check(lib().mk_set_schedule(self.h, mode))
+
+    def mk_graph_schedule(self):
+        """(order, offsets, est_us) of the static schedule, as numpy copies."""
+        o, f, w, est = (ctypes.POINTER(ctypes.c_uint32)(), ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_uint32(),
+                        ctypes.c_double())
+        _check(lib().mk_graph_schedule(self.h, ctypes.byref(o), ctypes.byref(f), ctypes.byref(w),
+                                       ctypes.byref(est)))
+        return _schedule_to_numpy(o, f, w.value), est.value
 
     def tasks_bytes(self) -> np.ndarray:
         p, n = ctypes.POINTER(MkTask)(), ctypes.c_uint32()

@@ -36,9 +36,11 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(16, os.cpu_count() or 4)
-    steps = [(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "lower.cpp"), "-o", os.path.join(OBJ, "lower.o")]),
-             (["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "runtime.hip"), "-o", os.path.join(OBJ, "runtime.o")])]
-    objs = [os.path.join(OBJ, "lower.o"), os.path.join(OBJ, "runtime.o")]
+    steps, objs = [], []
+    for src in ("lower.cpp", "schedule.cpp", "runtime.hip"):
+        o = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        steps.append(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     for name, args in specs():
         o = os.path.join(OBJ, f"kern_{name}.o")
         steps.append(["hipcc", *HIP_FLAGS, f"-DMK_SPEC_FN=ks_{name}", f"-DMK_SPEC_ARGS={args}", "-c",

@@ -45,7 +45,11 @@ struct Smem {
 
 struct LaunchArgs {
   const mk_task_t* tasks;
+  // Dependents array as uploaded, with bit 31 set on edges whose child is a NOP join
+  // (the CSR indices are unchanged; the flag saves a descriptor load per edge).
   const uint32_t* edges;
+  const uint32_t* order;      // static schedule: task lists grouped by workgroup
+  const uint32_t* order_off;  // [grid + 1]; null = dynamic tickets
   const uint64_t* table;
   uint32_t* arrivals;
   Ctrl* ctrl;
@@ -192,6 +196,49 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
   return sm.flag != 0;
 }
 
+// Count one arrival on each of the n dependents listed at edges[off].  A NOP join is
+// never run as a task: the parent whose increment completes its count (the returned
+// old value is the last one short of epoch * indeg) fires it on the spot, counting
+// one arrival on each of the NOP's own dependents.  NOP joins never feed NOP joins
+// (checked when lowering), so this recursion is one level deep.  Wave 0 only; the
+// caller has issued the release fence.
+__device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t off, uint32_t n) {
+  const int lane = lane_id();
+  for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    uint32_t fire = 0xFFFFFFFFu;
+    if (i < n) {
+      const uint32_t e = ldg<uint32_t>(a.edges, off + i);
+      const uint32_t c = e & 0x7FFFFFFFu;
+      MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + c;
+      if (e >> 31) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t indeg = ldg<uint32_t>(a.tasks, (size_t)c * 16 + 2);  // remaining_deps
+        if (old + 1u == a.epoch * indeg) fire = c;
+      } else {
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    uint64_t pending = __ballot(fire != 0xFFFFFFFFu);
+    while (pending) {
+      const int src = __builtin_ctzll(pending);
+      pending &= pending - 1;
+      const uint32_t c = __builtin_amdgcn_readlane(fire, src);
+      // Every other parent's data was released before its increment, which this wave
+      // has now observed; order that before the NOP's own releases.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t nd = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 3));
+      const uint32_t no = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 4));
+      for (uint32_t j = lane; j < nd; j += 64) {
+        const uint32_t cc = ldg<uint32_t>(a.edges, no + j) & 0x7FFFFFFFu;
+        __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + cc, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
 // Make this workgroup's writes visible at agent scope, then count one arrival on
 // every dependent.  Called by all threads after the task body.
 __device__ __forceinline__ void release_dependents(const LaunchArgs& a, const mk_task_t& d) {
@@ -199,11 +246,7 @@ __device__ __forceinline__ void release_dependents(const LaunchArgs& a, const mk
   __syncthreads();
   if (wave_id() == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t n = (uint32_t)d.num_dependents;
-    for (uint32_t i = lane_id(); i < n; i += 64) {
-      const uint32_t c = ldg<uint32_t>(a.edges, d.dependents_offset + i);
-      __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    signal_dependents(a, d.dependents_offset, (uint32_t)d.num_dependents);
   }
 }
 

@@ -70,10 +70,23 @@ struct Lowered {
 int validate_cfg(const mk_model_cfg* cfg);
 int lower(const mk_model_cfg* cfg, Lowered& out);
 
+// Static schedule: the non-NOP tasks split into one list per workgroup, each list in
+// increasing task order (so the topological-order deadlock argument holds per list).
+// Built by simulating list scheduling in emission order with a byte-count cost model:
+// each task goes to the workgroup that can start it earliest.  NOP joins get no
+// workgroup: their last-arriving parent fires them.
+struct Schedule {
+  std::vector<uint32_t> order;    // task indices, grouped by workgroup
+  std::vector<uint32_t> offsets;  // [workers + 1]
+  double est_us = 0;              // simulated step time (diagnostic)
+};
+void build_schedule(const Lowered& L, uint32_t workers, Schedule& out);
+
 int set_error(int code, const std::string& msg);
 
 }  // namespace mk
 
 struct mk_lowered {
   mk::Lowered low;
+  mk::Schedule sched;
 };

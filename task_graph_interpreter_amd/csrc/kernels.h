@@ -61,7 +61,7 @@ __device__ __forceinline__ void run_task_spec(const LaunchArgs& a, const mk_task
     case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
     case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
-    default: dep_wait(a, t, d.remaining_deps, sm); break;  // NOP join
+    default: break;  // NOP joins never run as tasks: their last parent fires them
   }
 }
 
@@ -88,18 +88,35 @@ __device__ __forceinline__ mk_task_t read_desc(const Smem& sm, int slot) {
   return d;
 }
 
-// The persistent interpreter.  Tickets are claimed one task ahead (the claim's round
-// trip and the next descriptor's fetch overlap the current task); descriptors and
-// tickets are double-buffered in LDS, which is safe because every iteration ends in a
-// workgroup barrier.  Each workgroup makes exactly one failing claim per step, so the
-// ticket counter advances by n_tasks + grid per step and never needs a reset.
-// Trace mode (a.trace != null) records per-task timestamps.
+// The next task of this workgroup: the next entry of its static list, or (dynamic
+// mode) the next ticket of the device-wide counter.  NOP joins are skipped: their
+// last-arriving parent fires them.  Thread 0 only.
+__device__ __forceinline__ uint32_t next_task(const LaunchArgs& a, uint32_t& pos, uint32_t end) {
+  if (a.order_off) return pos < end ? ldg<uint32_t>(a.order, pos++) : 0xFFFFFFFFu;
+  for (;;) {
+    const uint32_t t = claim_ticket(a);
+    if (t >= a.n_tasks) return 0xFFFFFFFFu;
+    if (ldg<uint16_t>(a.tasks, (size_t)t * 32) != MK_OP_NOP) return t;
+  }
+}
+
+// The persistent interpreter.  The next task is fetched one task ahead (the claim's
+// round trip, or the list read, and the descriptor fetch overlap the current task);
+// descriptors and task ids are double-buffered in LDS, which is safe because every
+// iteration ends in a workgroup barrier.  In dynamic mode each workgroup makes exactly
+// one failing claim per step, so the ticket counter advances by n_tasks + grid per
+// step and never needs a reset.  Trace mode (a.trace != null) records timestamps.
 template <class S>
 __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) {
   __shared__ Smem sm;
   const bool trace = a.trace != nullptr;
+  uint32_t pos = 0, end = 0;  // static list cursor (thread 0)
   if (threadIdx.x == 0) {
-    uint32_t t0 = claim_ticket(a);
+    if (a.order_off) {
+      pos = ldg<uint32_t>(a.order_off, blockIdx.x);
+      end = ldg<uint32_t>(a.order_off, blockIdx.x + 1);
+    }
+    uint32_t t0 = next_task(a, pos, end);
     if (read_status(a) != 0) t0 = 0xFFFFFFFFu;
     sm.ticket[0] = t0;
     if (t0 < a.n_tasks) stage_desc(a, t0, sm, 0);
@@ -113,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
     uint32_t nt = 0;
     if (threadIdx.x == 0) {
       if (trace) t_claim = clock100();
-      nt = claim_ticket(a);
+      nt = next_task(a, pos, end);
     }
     run_task_spec<S>(a, d, t, sm);
     uint64_t t_end = 0;

@@ -201,6 +201,12 @@ int validate_cfg(const mk_model_cfg* c) {
     if ((K * wes) % 16) return set_error(MK_ERR_INVALID, "GEMV inner dims must be multiples of 16 bytes");
     if (K > 32768) return set_error(MK_ERR_INVALID, "GEMV inner dim above 32768 (LDS staging)");
   }
+  // The GEMV addresses a weight matrix with 32-bit byte offsets.
+  const int64_t H = c->hidden;
+  const int64_t wbytes[5] = {qkv * H, H * (int64_t)c->n_q_heads * c->head_dim, 2ll * c->intermediate * H,
+                             H * (int64_t)c->intermediate, (int64_t)c->vocab * H};
+  for (int64_t e : wbytes)
+    if (e * wes >= (1ll << 32)) return set_error(MK_ERR_INVALID, "a weight matrix is 4 GiB or larger");
   const int64_t lpk = c->head_dim * kes / 16;
   if ((c->head_dim * kes) % 16 || lpk < 1 || lpk > 64 || (lpk & (lpk - 1)))
     return set_error(MK_ERR_INVALID, "head_dim * cache element size must be 16 * 2^j bytes, at most 1 KB");
@@ -413,6 +419,14 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
   }
   gemv(x, H, bi.w_lm(), V, MK_FLAG_RMS_NORM_INPUT, bi.final_norm(), bi.logits());
   bld.finish();
+  // A NOP join is fired inline by the parent that completes its count, which then
+  // counts arrivals on the NOP's own dependents without further checks: a NOP must
+  // never feed another NOP.
+  for (const mk_task_t& d : L.tasks)
+    if (d.op_id == MK_OP_NOP)
+      for (int32_t i = 0; i < d.num_dependents; ++i)
+        if (L.tasks[L.edges[d.dependents_offset + i]].op_id == MK_OP_NOP)
+          return set_error(MK_ERR_INVALID, "internal: a NOP join feeds another NOP join");
 
   BlobHeader& h = L.header;
   h.magic = 0x31474B4Du;  // "MKG1"

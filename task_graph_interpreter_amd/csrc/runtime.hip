@@ -70,7 +70,12 @@ struct mk_graph {
   uint32_t grid = 0;
   char* d_blob = nullptr;
   mk_task_t* d_tasks = nullptr;
-  uint32_t* d_edges = nullptr;
+  uint32_t* d_edges = nullptr;       // as lowered
+  uint32_t* d_edges_dev = nullptr;   // bit 31 set where the child is a NOP join
+  uint32_t* d_order = nullptr;       // static schedule lists
+  uint32_t* d_order_off = nullptr;   // [grid + 1]
+  mk::Schedule sched;
+  int sched_mode = MK_SCHED_STATIC;
   uint64_t* d_table = nullptr;
   uint32_t* d_arrivals = nullptr;
   mk::Ctrl* d_ctrl = nullptr;
@@ -110,7 +115,11 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   mk::LaunchArgs a;
   std::memset(&a, 0, sizeof(a));
   a.tasks = g->d_tasks;
-  a.edges = g->d_edges;
+  a.edges = g->d_edges_dev;
+  if (g->sched_mode == MK_SCHED_STATIC) {
+    a.order = g->d_order;
+    a.order_off = g->d_order_off;
+  }
   a.table = g->d_table;
   a.arrivals = g->d_arrivals;
   a.ctrl = g->d_ctrl;
@@ -237,20 +246,45 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
     if (L.scratch_off[i] != UINT64_MAX) table[i] = (uint64_t)(uintptr_t)scratch_dev + L.scratch_off[i];
   table[bi.logits()] = (uint64_t)mk::TAG_LOGITS << mk::kTagShift;
 
-  // One blob: 64-byte header, task array, edge array.
-  const size_t nt = L.tasks.size(), ne = L.edges.size();
-  const size_t blob_bytes = sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t) + ne * sizeof(uint32_t);
+  // Static schedule over one workgroup per CU.
+  try {
+    mk::build_schedule(L, g->grid, g->sched);
+  } catch (const std::bad_alloc&) {
+    return fail(mk::set_error(MK_ERR_NOMEM, "out of host memory while scheduling"));
+  }
+  const mk::Schedule& S = g->sched;
+
+  // One blob: 64-byte header, task array, edge array as lowered, the edge array the
+  // kernels read (NOP children flagged), the static lists and their offsets.
+  const size_t nt = L.tasks.size(), ne = L.edges.size(), no = S.order.size();
+  std::vector<uint32_t> flagged(L.edges);
+  for (uint32_t& c : flagged)
+    if (L.tasks[c].op_id == MK_OP_NOP) c |= 0x80000000u;
+  const size_t off_tasks = sizeof(mk::BlobHeader);
+  const size_t off_edges = off_tasks + nt * sizeof(mk_task_t);
+  const size_t off_flagged = off_edges + ne * 4;
+  const size_t off_order = off_flagged + ne * 4;
+  const size_t off_order_off = off_order + no * 4;
+  const size_t blob_bytes = off_order_off + S.offsets.size() * 4;
   std::vector<char> blob(blob_bytes);
   std::memcpy(blob.data(), &L.header, sizeof(mk::BlobHeader));
-  std::memcpy(blob.data() + sizeof(mk::BlobHeader), L.tasks.data(), nt * sizeof(mk_task_t));
-  if (ne) std::memcpy(blob.data() + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t), L.edges.data(), ne * 4);
+  std::memcpy(blob.data() + off_tasks, L.tasks.data(), nt * sizeof(mk_task_t));
+  if (ne) {
+    std::memcpy(blob.data() + off_edges, L.edges.data(), ne * 4);
+    std::memcpy(blob.data() + off_flagged, flagged.data(), ne * 4);
+  }
+  if (no) std::memcpy(blob.data() + off_order, S.order.data(), no * 4);
+  std::memcpy(blob.data() + off_order_off, S.offsets.data(), S.offsets.size() * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
   if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
   if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4)) != hipSuccess)
     return fail(hip_fail(e, "hipMalloc(arrivals)"));
   if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
-  g->d_tasks = (mk_task_t*)(g->d_blob + sizeof(mk::BlobHeader));
-  g->d_edges = (uint32_t*)(g->d_blob + sizeof(mk::BlobHeader) + nt * sizeof(mk_task_t));
+  g->d_tasks = (mk_task_t*)(g->d_blob + off_tasks);
+  g->d_edges = (uint32_t*)(g->d_blob + off_edges);
+  g->d_edges_dev = (uint32_t*)(g->d_blob + off_flagged);
+  g->d_order = (uint32_t*)(g->d_blob + off_order);
+  g->d_order_off = (uint32_t*)(g->d_blob + off_order_off);
   if ((e = hipMemcpyAsync(g->d_blob, blob.data(), blob_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     return fail(hip_fail(e, "hipMemcpyAsync(blob)"));
   if ((e = hipMemcpyAsync(g->d_table, table.data(), table.size() * 8, hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -284,6 +318,23 @@ int mk_graph_grid(const mk_graph* g, uint32_t* workgroups) {
 
 const char* mk_graph_kernel_name(const mk_graph* g) { return g && g->spec ? g->spec->name : ""; }
 
+int mk_set_schedule(mk_graph* g, int mode) {
+  if (!g || (mode != MK_SCHED_STATIC && mode != MK_SCHED_DYNAMIC))
+    return mk::set_error(MK_ERR_INVALID, "graph is NULL or unknown schedule mode");
+  g->sched_mode = mode;
+  return MK_OK;
+}
+
+int mk_graph_schedule(const mk_graph* g, const uint32_t** order, const uint32_t** offsets, uint32_t* workers,
+                      double* est_us) {
+  if (!g || !order || !offsets || !workers) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  *order = g->sched.order.data();
+  *offsets = g->sched.offsets.data();
+  *workers = g->grid;
+  if (est_us) *est_us = g->sched.est_us;
+  return MK_OK;
+}
+
 int mk_set_wait_limit(mk_graph* g, uint64_t ticks) {
   if (!g || ticks == 0) return mk::set_error(MK_ERR_INVALID, "graph is NULL or limit is 0");
   g->wait_limit = ticks;
@@ -312,7 +363,9 @@ int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const i
   hipError_t e = hipLaunchCooperativeKernel(g->kernels.persistent, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
   if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(interpreter)");
   g->epoch += 1;
-  g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
+  // Dynamic mode: every ticket is claimed once and every workgroup makes one failing
+  // claim; static mode leaves the counter alone.
+  if (g->sched_mode == MK_SCHED_DYNAMIC) g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
   g->last_stream = s;
   return MK_OK;
 }

@@ -62,6 +62,7 @@ def test_abi_mismatch_fails_loudly():
     (dict(gemv_config=1), "gemv_config"),
     (dict(head_dim=63), "head_dim"),
     (dict(kv_chunk=100_000), "kv_chunk"),
+    (dict(vocab=20_000_000), "4 GiB"),
 ])
 def test_invalid_configs_rejected(over, msg):
     cfg, keep = _cfg(workloads.tiny(), **over)

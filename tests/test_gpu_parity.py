@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import task_graph_interpreter_amd as mk
 from oracle import decode as od
 from oracle import graph as og
 from oracle.params import GeneratedParams
@@ -63,26 +64,44 @@ def test_tiny_step_all_activations(path):
     run.close()
 
 
+SCHED = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC}
+
+
 def test_persistent_equals_per_op_bitwise_and_is_repeatable():
     w = workloads.tiny()
-    _say("tiny persistent vs per-op bitwise, 5 repeats")
+    _say("tiny persistent (static and dynamic lists) vs per-op bitwise, 5 repeats each")
     run = MkRun(w)
     a = run.step("per_op")
-    for _ in range(5):
-        b = run.step("persistent")
-        assert np.array_equal(a, b)
+    for mode in ["static", "dynamic", "static"]:
+        run.graph.mk_set_schedule(SCHED[mode])
+        for _ in range(5):
+            b = run.step("persistent")
+            assert np.array_equal(a, b), mode
     run.close()
 
 
+def test_device_schedule_equals_host_schedule():
+    w = workloads.tiny()
+    _say("tiny schedule uploaded == host schedule")
+    run = MkRun(w)
+    (order, offsets), est = run.graph.mk_graph_schedule()
+    (horder, hoffsets), hest = run.lowered.schedule(run.graph.mk_graph_grid())
+    assert np.array_equal(order, horder) and np.array_equal(offsets, hoffsets) and est == hest
+    assert run.graph.mk_graph_kernel_name() == "tiny_f32"
+    run.close()
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
 @pytest.mark.parametrize("joins", [1, 0])
-def test_tiny_variants_bf16_batch_ragged(joins):
+def test_tiny_variants_bf16_batch_ragged(joins, mode):
     # bf16 weights and cache, 3 sequences of different lengths, GQA 8/2, tiles and
     # chunks that do not divide the sizes evenly.
     w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1, batch=3,
                                  kv_len=(128, 41, 97), n_q_heads=8, gemv_tiles=5, kv_chunk=24,
                                  join_nodes=joins, name="tiny_bf16_b3")
-    _say(f"tiny bf16 batch 3 ragged, joins={joins}")
+    _say(f"tiny bf16 batch 3 ragged, joins={joins}, {mode} lists")
     run = MkRun(w)
+    run.graph.mk_set_schedule(SCHED[mode])
     logits = run.step("persistent")
     ref, inter = _oracle(w, keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
@@ -128,13 +147,15 @@ def test_bad_position_reports_status_then_recovers():
     run.close()
 
 
-def test_wait_timeout_drains_and_recovers():
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_wait_timeout_drains_and_recovers(mode):
     # A 1-tick bound on every dependency wait: tasks whose producers are not done at
     # the first look give up, the step drains, mk_status reports a timeout, and the
     # next step with the normal bound is correct again.
     w = workloads.tiny()
-    _say("tiny forced wait timeout")
+    _say(f"tiny forced wait timeout, {mode} lists")
     run = MkRun(w)
+    run.graph.mk_set_schedule(SCHED[mode])
     good = run.step("persistent")
     run.graph.mk_set_wait_limit(1)
     run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
@@ -146,23 +167,41 @@ def test_wait_timeout_drains_and_recovers():
     run.close()
 
 
-def test_trace_mode_records_every_task():
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_trace_mode_records_every_task(mode):
     w = workloads.tiny()
-    _say("tiny trace mode")
+    _say(f"tiny trace mode, {mode} lists")
     run = MkRun(w)
+    run.graph.mk_set_schedule(SCHED[mode])
     n = run.plan["n_tasks"]
     trace = torch.zeros(n * 8, dtype=torch.int64, device="cuda")
     run.graph.mk_set_trace(trace.data_ptr())
     run.step("persistent")
     run.graph.mk_set_trace(None)
     tr = trace.cpu().numpy().reshape(n, 8)
-    assert (tr[:, 1] > 0).all()
-    assert (tr[:, 1] <= tr[:, 2]).all() and (tr[:, 2] <= tr[:, 3]).all() and (tr[:, 3] <= tr[:, 4]).all()
     tasks, edges = og.build_graph(w)
+    nop = tasks["op_id"] == 0
+    assert nop.any(), "the tiny graph has NOP joins"
+    assert (tr[nop] == 0).all(), "NOP joins never run as tasks"
+    run_ = ~nop
+    assert (tr[run_, 1] > 0).all()
+    t1, t2, t3, t4 = (tr[run_, i] for i in (1, 2, 3, 4))
+    assert (t1 <= t2).all() and (t2 <= t3).all() and (t3 <= t4).all()
+    if mode == "static":  # each workgroup runs its list in order, on one CU
+        (order, offsets), _ = run.graph.mk_graph_schedule()
+        for i in range(len(offsets) - 1):
+            lst = order[offsets[i]:offsets[i + 1]]
+            assert len(set(tr[lst, 0].tolist())) <= 1
+            assert (np.diff(tr[lst, 1]) >= 0).all()
     par = og.parents_from_csr(tasks, edges)
-    for t in range(n):  # a task becomes ready only after every parent ended
+
+    def ends(p):  # when a parent's data was complete: a NOP's parents' ends
+        return [tr[p, 3]] if not nop[p] else [e for q in par[p] for e in ends(q)]
+
+    for t in np.flatnonzero(run_):  # a task becomes ready only after every parent ended
         for p in par[t]:
-            assert tr[p, 3] <= tr[t, 2] + 1, (p, t)
+            for e in ends(p):
+                assert e <= tr[t, 2] + 1, (p, t)
     run.close()
 
 
