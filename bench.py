@@ -96,6 +96,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
     ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
+    ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
     ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
                     help="how persistent workgroups find tasks: host-built lists or a ticket counter")
     args = ap.parse_args()
@@ -115,6 +116,8 @@ def main():
     from synth.device import DeviceInputs
 
     w = workloads.get(args.workload)
+    if args.kv_chunk:
+        w = w.replace(kv_chunk=args.kv_chunk)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
     inp = DeviceInputs(w)

@@ -1,7 +1,7 @@
 // Device-side shared pieces of the interpreter: launch arguments, buffer-table
 // resolution, explicit global-memory accessors, bf16 conversion, wavefront
-// reductions, and the readiness protocol (acquire-wait on a task's own counter,
-// release-increment of each dependent's).
+// reductions, and the readiness protocol (wait on a task's own counter, then count
+// one arrival on each dependent's, with device-scope accesses for the shared data).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,6 +82,54 @@ __device__ __forceinline__ void stg(void* p, size_t i, T v) {
   ((MK_GLOBAL T*)p)[i] = v;
 }
 
+// Device-scope accesses, for the data one task writes and another task reads within
+// the same step (activations, attention partials, the new token's cache row).
+//
+// The MI355X has one L2 per XCD and the L2s are not kept coherent with each other.
+// The fence-based protocol (a release fence before the counter increment, an acquire
+// fence after the counter wait) costs a whole-L2 writeback (buffer_wbl2) on every
+// release and a whole-L2 invalidate (buffer_inv) on every acquire, and the writebacks
+// of the workgroups of one XCD serialise: under a wide matmul's 256 simultaneous
+// releases one release took 5-20 us.  Instead, every access to in-step shared data is
+// an agent-scope relaxed atomic, which the compiler emits as a global load/store with
+// the device-scope cache-policy bit (sc1): the store is written through to the
+// device's coherence point before it is acknowledged, and the load is served from
+// there.  Ordering then needs no cache maintenance: the producer waits for its stores
+// to be acknowledged (s_waitcnt vmcnt(0)) before its counter increments, and the
+// consumer issues its loads only after it has observed its counter.  Plain
+// (CU-scope) loads are kept for data no task of the step writes: weights, norm
+// gammas, the embedding, tokens, positions and the cache rows of earlier steps
+// (kernel boundaries make those coherent).
+template <typename T>
+__device__ __forceinline__ T ld_dev(const void* p, size_t i) {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8, "scalar device-scope load");
+  return __hip_atomic_load((const MK_GLOBAL T*)p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(void* p, size_t i, T v) {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8, "scalar device-scope store");
+  __hip_atomic_store((MK_GLOBAL T*)p + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at p + 16 * i4, as two 8-byte device-scope loads.
+__device__ __forceinline__ u32x4 ld_dev_u4(const void* p, size_t i4) {
+  const uint64_t lo = ld_dev<uint64_t>(p, 2 * i4), hi = ld_dev<uint64_t>(p, 2 * i4 + 1);
+  u32x4 r;
+  r.x = (uint32_t)lo;
+  r.y = (uint32_t)(lo >> 32);
+  r.z = (uint32_t)hi;
+  r.w = (uint32_t)(hi >> 32);
+  return r;
+}
+__device__ __forceinline__ f32x4 ld_dev_f4(const void* p, size_t i4) {
+  const u32x4 u = ld_dev_u4(p, i4);
+  f32x4 r;
+  r.x = __uint_as_float(u.x);
+  r.y = __uint_as_float(u.y);
+  r.z = __uint_as_float(u.z);
+  r.w = __uint_as_float(u.w);
+  return r;
+}
+
 // Wave index as a wave-uniform (scalar) value, so branches on it stay scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -138,9 +186,34 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return v;
 }
 
-// Sum across groups of `width` lanes (width a power of two <= 64).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum across aligned groups of `width` lanes (a wave-uniform power of two <= 64),
+// leaving the group's total in every lane of the group.  Up to 16 lanes this is a
+// butterfly of DPP moves (VALU only, no LDS round trip): quad_perm [1,0,3,2] and
+// [2,3,0,1] sum each quad, row_half_mirror pairs the two quads of each 8 lanes,
+// row_mirror the two halves of each 16.  Wider groups finish with xor shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_swap_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return v + __int_as_float(s);
+}
+template <int W>
+__device__ __forceinline__ float group_allsum(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v = dpp_swap_add<0xB1>(v);
+  if constexpr (W >= 4) v = dpp_swap_add<0x4E>(v);
+  if constexpr (W >= 8) v = dpp_swap_add<0x141>(v);
+  if constexpr (W >= 16) v = dpp_swap_add<0x140>(v);
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+__device__ __forceinline__ float group_allsum(float v, int width) {
+  if (width >= 2) v = dpp_swap_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (width >= 4) v = dpp_swap_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (width >= 8) v = dpp_swap_add<0x141>(v);  // row_half_mirror
+  if (width >= 16) v = dpp_swap_add<0x140>(v); // row_mirror
+  if (width >= 32) v += __shfl_xor(v, 16, 64);
+  if (width >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 
@@ -157,10 +230,12 @@ __device__ __forceinline__ uint32_t read_status(const LaunchArgs& a) {
 }
 
 // Wait until task t's counter shows all of this step's parents have arrived
-// (arrivals[t] - epoch * indeg >= 0 in wrapping 32-bit arithmetic), then acquire at
-// agent scope so every wave of the workgroup sees the producers' writes.  Bounded:
-// on timeout (or if another workgroup raised an error) the step is abandoned.
-// Returns false if the step was abandoned.  Called by all threads.
+// (arrivals[t] - epoch * indeg >= 0 in wrapping 32-bit arithmetic).  The producers'
+// data was written at device scope and acknowledged before their increments, and
+// every wave reads it with device-scope loads issued after the closing barrier, so
+// no cache invalidate is needed.  Bounded: on timeout (or if another workgroup raised
+// an error) the step is abandoned.  Returns false if the step was abandoned.  Called
+// by all threads.
 __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_t indeg, Smem& sm) {
   if (indeg == 0) {
     if (threadIdx.x == 0) sm.t_ready = clock100();
@@ -188,7 +263,6 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     sm.flag = ok;
     sm.t_ready = clock100();
   }
@@ -201,7 +275,7 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
 // old value is the last one short of epoch * indeg) fires it on the spot, counting
 // one arrival on each of the NOP's own dependents.  NOP joins never feed NOP joins
 // (checked when lowering), so this recursion is one level deep.  Wave 0 only; the
-// caller has issued the release fence.
+// caller has waited for its own data stores to be acknowledged.
 __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t off, uint32_t n) {
   const int lane = lane_id();
   for (uint32_t i0 = 0; i0 < n; i0 += 64) {
@@ -224,10 +298,8 @@ __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t 
       const int src = __builtin_ctzll(pending);
       pending &= pending - 1;
       const uint32_t c = __builtin_amdgcn_readlane(fire, src);
-      // Every other parent's data was released before its increment, which this wave
-      // has now observed; order that before the NOP's own releases.
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      // Every other parent's data reached the device coherence point before its
+      // increment, and those increments precede this one on the NOP's counter.
       const uint32_t nd = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 3));
       const uint32_t no = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 4));
       for (uint32_t j = lane; j < nd; j += 64) {
@@ -239,15 +311,14 @@ __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t 
   }
 }
 
-// Make this workgroup's writes visible at agent scope, then count one arrival on
-// every dependent.  Called by all threads after the task body.
+// Wait until every device-scope store of the workgroup is acknowledged (written
+// through to the device coherence point), then count one arrival on every
+// dependent.  The asm's memory clobber and the barrier keep the compiler from moving
+// any store past the increments.  Called by all threads after the task body.
 __device__ __forceinline__ void release_dependents(const LaunchArgs& a, const mk_task_t& d) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (wave_id() == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    signal_dependents(a, d.dependents_offset, (uint32_t)d.num_dependents);
-  }
+  if (wave_id() == 0) signal_dependents(a, d.dependents_offset, (uint32_t)d.num_dependents);
 }
 
 }  // namespace mk

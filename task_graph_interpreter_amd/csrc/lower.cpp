@@ -213,6 +213,10 @@ int validate_cfg(const mk_model_cfg* c) {
   const int64_t grp = c->n_q_heads / c->n_kv_heads;
   if (grp * (c->head_dim + c->kv_chunk) + 8 * std::min<int64_t>(grp, 8) * c->head_dim > 32768)
     return set_error(MK_ERR_INVALID, "kv_chunk too large for the attention partial's LDS");
+  // The combine stages every chunk's (m, l) for the group's heads in LDS.
+  const int64_t max_chunks = ((int64_t)c->kv_capacity + c->kv_chunk - 1) / c->kv_chunk;
+  if (max_chunks * grp * 2 > 32768 || 2 * grp > 1024)
+    return set_error(MK_ERR_INVALID, "too many KV chunks per head group for the combine's LDS (raise kv_chunk)");
   if (c->batch > (1 << 20) || c->kv_capacity > (1 << 30)) return set_error(MK_ERR_INVALID, "size too large");
   return MK_OK;
 }

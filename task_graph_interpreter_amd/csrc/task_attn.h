@@ -9,10 +9,11 @@
 namespace mk {
 
 // ---------------------------------------------------------------------------------
-// ATTENTION_APPEND ("RoPE-append current k,v"): for sequence b and KV head g, rotate
-// the group's query heads and k_g (rotate-half RoPE, angle pos * theta^(-2i/hd) with
-// the angle and its sine/cosine evaluated in fp64), write rotated q to q_rot and the
-// rotated k and v into cache slot positions[b], rounded to the cache dtype.
+// ATTENTION_APPEND (OpId 7 of the OpId table in "Mega kernel initial"): for sequence
+// b and KV head g, rotate the group's query heads and k_g (rotate-half RoPE, angle
+// pos * theta^(-2i/hd) with the angle and its sine/cosine evaluated in fp64), write
+// rotated q to q_rot and the rotated k and v into cache slot positions[b], rounded
+// to the cache dtype.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void rope_cs(int pos, int i, int hd, float theta, float& c, float& s) {
   const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
@@ -54,44 +55,45 @@ __device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t
       float c = cs_c, s = cs_s;
       if (e != e0) rope_cs(pos, i, hd, a.rope_theta, c, s);
       const size_t src = hh < hc ? row + (size_t)(h0 + hh) * hd : row + (size_t)(Hq + g) * hd;
-      const float x0 = ldg<float>(qkv, src + i), x1 = ldg<float>(qkv, src + i + half);
+      const float x0 = ld_dev<float>(qkv, src + i), x1 = ld_dev<float>(qkv, src + i + half);
       const float r0 = x0 * c - x1 * s;
       const float r1 = x1 * c + x0 * s;
       if (hh < hc) {
         const size_t dst = (size_t)b * Hq * hd + (size_t)(h0 + hh) * hd;
-        stg<float>(qrot, dst + i, r0);
-        stg<float>(qrot, dst + i + half, r1);
+        st_dev<float>(qrot, dst + i, r0);
+        st_dev<float>(qrot, dst + i + half, r1);
       } else if (bf16) {
-        stg<uint16_t>(kc, slot + i, f32_to_bf16_rne(r0));
-        stg<uint16_t>(kc, slot + i + half, f32_to_bf16_rne(r1));
+        st_dev<uint16_t>(kc, slot + i, f32_to_bf16_rne(r0));
+        st_dev<uint16_t>(kc, slot + i + half, f32_to_bf16_rne(r1));
       } else {
-        stg<float>(kc, slot + i, r0);
-        stg<float>(kc, slot + i + half, r1);
+        st_dev<float>(kc, slot + i, r0);
+        st_dev<float>(kc, slot + i + half, r1);
       }
     } else {
       const int i = e - nrot;
-      const float v = ldg<float>(qkv, row + (size_t)(Hq + Hkv + g) * hd + i);
-      if (bf16) stg<uint16_t>(vc, slot + i, f32_to_bf16_rne(v));
-      else stg<float>(vc, slot + i, v);
+      const float v = ld_dev<float>(qkv, row + (size_t)(Hq + Hkv + g) * hd + i);
+      if (bf16) st_dev<uint16_t>(vc, slot + i, f32_to_bf16_rne(v));
+      else st_dev<float>(vc, slot + i, v);
     }
   }
 }
 
 // ---------------------------------------------------------------------------------
-// ATTENTION_PARTIAL ("online-softmax over one KV chunk -> (m,l,o) scratch"): keys
+// ATTENTION_PARTIAL (OpId 8 of the same table): keys
 // [c*chunk, min((c+1)*chunk, positions[b]+1)) of KV head g, for the group's q heads.
 //   s_j = q.k_j / sqrt(hd); m = max s; l = sum e^(s-m); o = sum e^(s-m) v_j
 // (o unnormalised; an empty chunk gives (-inf, 0, 0)).  Slot layout [heads][hd + 2]:
 // o in [0, hd), m at hd, l at hd + 1.
 //
 // A key row is read by a group of hd*es/16 lanes (16 bytes each); the rows of the
-// chunk are spread over the workgroup in rounds.  Rows older than the new token are
-// static, so up to kPartRounds rounds of K and V are loaded before the dependency
-// wait; the new token's row (written by this step's APPEND) is read after it.  Each
-// lane group keeps a running (m, l, o) per head; groups are merged with the same
-// log-sum-exp rule across the wavefront (xor shuffles) and across wavefronts (LDS).
+// chunk are spread over the workgroup in rounds, processed in double-buffered
+// batches of R rounds.  Rows older than the new token are static, so the first batch
+// is loaded before the dependency wait; the new token's row (written by this step's
+// APPEND) is read after it and folded in last.  Each lane group keeps a running
+// (m, l, o) per head (the dot product is summed across the group with DPP moves);
+// groups are merged with the same log-sum-exp rule across the wavefront (xor
+// shuffles) and across wavefronts (LDS).
 // ---------------------------------------------------------------------------------
-constexpr int kPartRounds = 8;
 
 __device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2, float l2, const float* o2,
                                           int n) {
@@ -116,11 +118,10 @@ __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
 
 // One pass over the chunk for query heads [hg, hg + HM) of the group; the first pass
 // (hg == 0) prefetches before waiting on the producers.
-template <bool BF16, int HM>
+template <bool BF16, int HM, int LPK, int R>
 __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, int hg) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VEC = 16 / ES;
-  constexpr int R = kPartRounds;
   const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc_all = (int)d.reserved[2];
   const int c = (int)d.reserved[3], base = (int)d.reserved[4];
   const int g = d.k, hd = d.n, chunk = d.kv_len, nchunks = d.m;
@@ -144,20 +145,25 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   const int jnew = pos - lo;  // row of the new token (if inside this chunk)
 
   const int lane = lane_id(), wave = wave_id();
-  const int lpk = rowq, kpw = 64 / lpk, kpr = kWaves * kpw;
+  const int lpk = LPK > 0 ? LPK : rowq, kpw = 64 / lpk, kpr = kWaves * kpw;
   const int kl = lane / lpk, dl = lane % lpk;
   const int jbase = wave * kpw + kl;  // this lane group's row in round 0
   const int rounds = (n + kpr - 1) / kpr;
   const bool first = hg == 0;
-  auto row_idx = [&](int j) { return head_off + (size_t)(lo + j) * rowq + dl; };
+  // Rows past the chunk's end are clamped to its last row (loaded, then masked), so
+  // every load below is unconditional within a wave-uniform branch.
+  const int jmax = n > 0 ? n - 1 : 0;
+  auto row_idx = [&](int j) { return head_off + (size_t)(lo + (j < jmax ? j : jmax)) * rowq + dl; };
 
+  // Rows of earlier steps never change during the step: the first R rounds are
+  // loaded before the dependency wait.  The new token's row is loaded too but masked
+  // (it is stale until this step's APPEND has run) and folded in after the loop.
   u32x4 kr[R], vr[R];
+  if (rounds > 0) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int j = jbase + r * kpr;
-    if (r < rounds && j < n && (j != jnew || !first)) {
-      kr[r] = ldg<u32x4>(kc, row_idx(j));
-      vr[r] = ldg<u32x4>(vc, row_idx(j));
+    for (int r = 0; r < R; ++r) {
+      kr[r] = ldg<u32x4>(kc, row_idx(jbase + r * kpr));
+      vr[r] = ldg<u32x4>(vc, row_idx(jbase + r * kpr));
     }
   }
   if (first) {
@@ -173,10 +179,10 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   for (int h = 0; h < HM; ++h) {
     if (h < hc) {
       const size_t q4 = ((size_t)b * Hq * hd + (size_t)(h0 + hg + h) * hd + dl * VEC) / 4;
-      const f32x4 q0 = ldg<f32x4>(qrot, q4);
+      const f32x4 q0 = ld_dev_f4(qrot, q4);
       q[h][0] = q0.x * scale; q[h][1] = q0.y * scale; q[h][2] = q0.z * scale; q[h][3] = q0.w * scale;
       if (VEC == 8) {
-        const f32x4 q1 = ldg<f32x4>(qrot, q4 + 1);
+        const f32x4 q1 = ld_dev_f4(qrot, q4 + 1);
         q[h][4] = q1.x * scale; q[h][5] = q1.y * scale; q[h][6] = q1.z * scale; q[h][7] = q1.w * scale;
       } else {
         q[h][4] = q[h][5] = q[h][6] = q[h][7] = 0.f;
@@ -191,50 +197,60 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
-  for (int r0 = 0; r0 < rounds; r0 += R) {
-    if (r0 > 0) {
+  // Score one row against the heads and fold it into the running (m, l, o) of the
+  // lanes where `ok` holds (every lane of a group gets the group's full dot product).
+  auto fold = [&](const u32x4 kv, const u32x4 vv, bool ok) {
+    float kf[8], vf[8];
+    unpack<BF16>(kv, kf);
+    unpack<BF16>(vv, vf);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int j = jbase + (r0 + r) * kpr;
-        if (r0 + r < rounds && j < n) {
-          kr[r] = ldg<u32x4>(kc, row_idx(j));
-          vr[r] = ldg<u32x4>(vc, row_idx(j));
-        }
+    for (int h = 0; h < HM; ++h) {
+      if (h < hc) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s = fmaf(kf[e], q[h][e], s);
+        if constexpr (LPK > 0) s = group_allsum<LPK>(s);
+        else s = group_allsum(s, lpk);
+        // Branch-free online-softmax step; a masked lane keeps (m, l, o) unchanged.
+        const float mn = ok ? fmaxf(m[h], s) : m[h];
+        const float al = (m[h] == mn) ? 1.f : __expf(m[h] - mn);  // m = -inf -> 0
+        const float p = ok ? __expf(s - mn) : 0.f;
+        l[h] = fmaf(l[h], al, p);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(o[h][e], al, p * vf[e]);
+        m[h] = mn;
       }
+    }
+  };
+  // Batches of R rounds, double-buffered: the next batch's loads are issued before
+  // the current batch is folded.  All loads are unconditional (clamped rows; the
+  // last batch's look-ahead re-reads the chunk's last row), so the compiler can keep
+  // 2R rounds in flight with counted waits.
+  const int nbatch = (rounds + R - 1) / R;
+  for (int bt = 0; bt < nbatch; ++bt) {
+    u32x4 kn[R], vn[R];
+    const int jn = jbase + (bt + 1) * R * kpr;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      kn[r] = ldg<u32x4>(kc, row_idx(jn + r * kpr));
+      vn[r] = ldg<u32x4>(vc, row_idx(jn + r * kpr));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r0 + r < rounds) {
-        const int j = jbase + (r0 + r) * kpr;
-        const bool ok = j < n;
-        u32x4 kv = kr[r], vv = vr[r];
-        if (first && r0 == 0 && ok && j == jnew) {  // new token's row, written by this step's APPEND
-          kv = ldg<u32x4>(kc, row_idx(j));
-          vv = ldg<u32x4>(vc, row_idx(j));
-        }
-        float kf[8], vf[8];
-        unpack<BF16>(kv, kf);
-        unpack<BF16>(vv, vf);
-#pragma unroll
-        for (int h = 0; h < HM; ++h) {
-          if (h < hc) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) s = fmaf(kf[e], q[h][e], s);
-            s = group_sum(s, lpk);
-            if (ok) {
-              const float mn = fmaxf(m[h], s);
-              const float al = __expf(m[h] - mn);  // m = -inf -> 0
-              const float p = __expf(s - mn);
-              l[h] = fmaf(l[h], al, p);
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(o[h][e], al, p * vf[e]);
-              m[h] = mn;
-            }
-          }
-        }
-      }
+      const int j = jbase + (bt * R + r) * kpr;
+      fold(kr[r], vr[r], j < n && j != jnew);
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      kr[r] = kn[r];
+      vr[r] = vn[r];
+    }
+  }
+  // The new token's row, written by this step's APPEND: device-scope loads after the
+  // wait; lane group 0 of wave 0 folds it in.
+  if (jnew >= 0 && jnew < n) {
+    const size_t rn = head_off + (size_t)pos * rowq + dl;
+    fold(ld_dev_u4(kc, rn), ld_dev_u4(vc, rn), wave == 0 && kl == 0);
   }
   // Merge the lane groups of the wavefront (offsets lpk .. 32).
   for (int off = lpk; off < 64; off <<= 1) {
@@ -278,20 +294,38 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
       if (dd < hd) acc = fmaf(pw[dd], al, acc);
       else if (dd == hd + 1) acc = fmaf(pw[hd + 1], al, acc);
     }
-    stg<float>(out, out0 + h * stride + dd, (dd == hd) ? M : acc);
+    st_dev<float>(out, out0 + h * stride + dd, (dd == hd) ? M : acc);
   }
   return true;
 }
 
-template <bool KVBF16>
-__device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+template <bool KVBF16, int LPK, int R>
+__device__ __forceinline__ void partial_heads(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   const int hc = (int)d.reserved[2];
   for (int hg = 0; hg < hc; hg += 4)
-    if (!partial_pass<KVBF16, 4>(a, d, t, sm, hg)) return;
+    if (!partial_pass<KVBF16, 4, LPK, R>(a, d, t, sm, hg)) return;
+}
+
+// Lanes per cache row (head_dim * element size / 16) as a compile-time constant for
+// the common shapes (head_dim 64 and 128), else a run-time value.
+template <bool KVBF16>
+__device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  // R rounds per batch: 2 for chunks of at most two rounds, else 4.
+  const int lpk = d.n * (KVBF16 ? 2 : 4) / 16;
+  const bool short_chunk = d.kv_len <= 2 * kWaves * (64 / lpk);
+  if (lpk == 8) {
+    if (short_chunk) partial_heads<KVBF16, 8, 2>(a, d, t, sm);
+    else partial_heads<KVBF16, 8, 4>(a, d, t, sm);
+  } else if (lpk == 16) {
+    if (short_chunk) partial_heads<KVBF16, 16, 2>(a, d, t, sm);
+    else partial_heads<KVBF16, 16, 4>(a, d, t, sm);
+  } else {
+    partial_heads<KVBF16, 0, 4>(a, d, t, sm);
+  }
 }
 
 // ---------------------------------------------------------------------------------
-// ATTENTION_COMBINE ("LSE-merge of the partials -> final O"): per head,
+// ATTENTION_COMBINE (OpId 9 of the same table): per head,
 // M = max_c m_c, w_c = e^(m_c - M), O = sum_c w_c o_c / sum_c w_c l_c.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
@@ -300,20 +334,53 @@ __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_
   const float* part = (const float*)resolve(a, d.in_buf[0]);
   float* att = (float*)resolve(a, d.out_buf);
   if (!dep_wait(a, t, d.remaining_deps, sm)) return;
-  const int Hq = a.n_q_heads;
+  const int Hq = a.n_q_heads, stride = hd + 2, np = nch * hc;
+  // Slot (chunk c, head h) of this group is partials[(base + c) * hc + h].
+  // 1. Every (m, l) into LDS: [np][2].
+  float* ml = sm.xs;
+  for (int i = threadIdx.x; i < np; i += kThreads) {
+    const size_t s = ((size_t)base * hc + i) * stride + hd;
+    ml[2 * i] = ld_dev<float>(part, s);
+    ml[2 * i + 1] = ld_dev<float>(part, s + 1);
+  }
+  __syncthreads();
+  // 2. Per head: M = max_c m_c and lam = sum_c e^(m_c - M) l_c.
+  float* Mh = sm.red;  // [hc] max, then [hc] lam
+  if (threadIdx.x < hc) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * (c * hc + h)]);
+    float lam = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float m = ml[2 * (c * hc + h)];
+      lam = fmaf(m == -INFINITY ? 0.f : __expf(m - M), ml[2 * (c * hc + h) + 1], lam);
+    }
+    Mh[h] = M;
+    Mh[hc + h] = lam;
+  }
+  __syncthreads();
+  // 3. Weights w_c = e^(m_c - M) in place of m.
+  for (int i = threadIdx.x; i < np; i += kThreads) {
+    const float m = ml[2 * i];
+    ml[2 * i] = m == -INFINITY ? 0.f : __expf(m - Mh[i % hc]);
+  }
+  __syncthreads();
+  // 4. O[h][dd] = sum_c w_c o_c[dd] / lam, eight chunks' loads in flight at a time.
   for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
     const int h = e / hd, dd = e % hd;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ldg<float>(part, ((size_t)(base + c) * hc + h) * (hd + 2) + hd));
-    float lam = 0.f, o = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const size_t s = ((size_t)(base + c) * hc + h) * (hd + 2);
-      const float m = ldg<float>(part, s + hd);
-      const float w = m == -INFINITY ? 0.f : __expf(m - M);
-      lam = fmaf(w, ldg<float>(part, s + hd + 1), lam);
-      o = fmaf(w, ldg<float>(part, s + dd), o);
+    float o = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u < nch ? c0 + u : nch - 1;
+        v[u] = ld_dev<float>(part, ((size_t)(base + c) * hc + h) * stride + dd);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nch) o = fmaf(ml[2 * ((c0 + u) * hc + h)], v[u], o);
     }
-    stg<float>(att, (size_t)b * Hq * hd + (size_t)(h0 + h) * hd + dd, o / lam);
+    st_dev<float>(att, (size_t)b * Hq * hd + (size_t)(h0 + h) * hd + dd, o / Mh[hc + h]);
   }
 }
 

@@ -95,7 +95,7 @@ __device__ __forceinline__ void gemv_stage(const float* x, const char* gamma, bo
     if (b < nb) {
       f32x4* xo = (f32x4*)(sm.xs + b * K);
       for (int k4 = threadIdx.x; k4 < K4; k4 += kThreads) {
-        f32x4 v = ldg<f32x4>(x, (size_t)(b0 + b) * K4 + k4);
+        f32x4 v = ld_dev_f4(x, (size_t)(b0 + b) * K4 + k4);
         if (norm) {
           ss[b] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[b]))));
           float g0, g1, g2, g3;
@@ -155,7 +155,7 @@ __device__ __forceinline__ void gemv_flush(const GemvGeom& g, const float park[B
         const int j = g.silu ? (q >> 1) : q;
         const int c = g.c0 + g.wave + kWaves * j;
         const size_t o = (size_t)(b0 + b) * N + c;
-        stg<float>(y, o, v + (resid ? ldg<float>(res, o) : 0.f));
+        st_dev<float>(y, o, v + (resid ? ld_dev<float>(res, o) : 0.f));
       }
     }
   }

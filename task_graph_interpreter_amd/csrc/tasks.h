@@ -31,7 +31,7 @@ __device__ __forceinline__ void task_memcpy(const LaunchArgs& a, const mk_task_t
       float v;
       if (d.config_id == MK_DTYPE_BF16) v = __uint_as_float((uint32_t)ldg<uint16_t>(E, (size_t)tok * H + k) << 16);
       else v = ldg<float>(E, (size_t)tok * H + k);
-      stg<float>(x0, (size_t)b * H + k, v);
+      st_dev<float>(x0, (size_t)b * H + k, v);
     }
   }
 }
