@@ -33,9 +33,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_layers=(1, 2)):
+def cpu_baseline(w, budget_layers=(1, 2), min_seconds=6.0):
     """The oracle (float64 numpy) timed on this host on a bounded sample: the full step
-    with 1 and with 2 layers (same shapes, weights generated beforehand), extrapolated
+    with 1 and with 2 layers (same shapes, weights generated beforehand), each repeated
+    until about min_seconds of oracle work is timed (median per step), extrapolated
     linearly to the workload's layer count."""
     from threadpoolctl import threadpool_info
 
@@ -59,7 +60,7 @@ def cpu_baseline(w, budget_layers=(1, 2)):
         def cache(self, *a):
             return self.p.cache(*a)
 
-    times = {}
+    times, reps = {}, {}
     for nl in budget_layers:
         ws = w.replace(n_layers=nl)
         p = GeneratedParams(ws, backend="c")
@@ -72,9 +73,14 @@ def cpu_baseline(w, budget_layers=(1, 2)):
                 for g in range(ws.n_kv_heads):
                     for which in (0, 1):
                         pre.p.cache(l, which, b, g, 1)
-        t0 = time.perf_counter()
-        od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
-        times[nl] = time.perf_counter() - t0
+        # repeat the step until about min_seconds of oracle work is timed; median
+        runs = []
+        while sum(runs) < min_seconds or len(runs) < 3:
+            t0 = time.perf_counter()
+            od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
+            runs.append(time.perf_counter() - t0)
+        times[nl] = float(np.median(runs))
+        reps[nl] = len(runs)
         del pre, kv
     per_layer = times[2] - times[1]
     fixed = times[1] - per_layer
@@ -82,9 +88,75 @@ def cpu_baseline(w, budget_layers=(1, 2)):
     blas = [i.get("num_threads", 1) for i in threadpool_info()]
     cores = max([1] + blas)
     return {"value": w.batch / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float64 numpy oracle, full step of the same shapes with 1 layer ({times[1]:.2f} s) and "
-                       f"2 layers ({times[2]:.2f} s), extrapolated to {w.n_layers} layers = {est:.2f} s/step"),
+            "sample": (f"float64 numpy oracle, full step of the same shapes with 1 layer (median {times[1]:.3f} s "
+                       f"of {reps[1]} runs) and 2 layers (median {times[2]:.3f} s of {reps[2]} runs), "
+                       f"extrapolated to {w.n_layers} layers = {est:.2f} s/step"),
             "seconds_per_step_estimate": est}
+
+
+KERNEL_SRC = os.path.join(ROOT, "task_graph_interpreter_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP kernel sources: a traffic figure taken from hardware counters
+    is only reported while the kernels are the ones it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC)):
+        if name.endswith((".h", ".hip", ".cpp", ".def")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_interpreter_{workload}.json")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per persistent-kernel launch from the committed counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str, command: str) -> dict:
+    """Per-launch HBM traffic of the persistent kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
+    counter reads for a plain copy of copy_bytes (read once, written once)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row["Kernel_Name"]
+                    key = "interpreter" if "interpreter_kernel" in name else "copy" if "copy16_kernel" in name else None
+                    if key:
+                        vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fv, wv = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    f_int, w_int = float(np.median(fv["interpreter"])), float(np.median(wv["interpreter"]))
+    f_cp, w_cp = float(np.median(fv["copy"])), float(np.median(wv["copy"]))
+    kf, kw = copy_bytes / (f_cp * 1024.0), copy_bytes / (w_cp * 1024.0)
+    return {"workload": workload, "kernel": "interpreter_kernel", "kernel_source_hash": kernel_source_hash(),
+            "fetch_kib_per_launch": f_int, "write_kib_per_launch": w_int,
+            "copy_bytes": copy_bytes, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
+            "fetch_scale": kf, "write_scale": kw,
+            "traffic_bytes_per_launch": f_int * 1024.0 * kf + w_int * 1024.0 * kw,
+            "launches": [len(fv["interpreter"]), len(wv["interpreter"])], "command": command}
 
 
 def main():
@@ -95,12 +167,25 @@ def main():
     ap.add_argument("--workload", default="8b_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
+    ap.add_argument("--no-alt-schedule", action="store_true", help="skip timing the other schedule mode")
     ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (byte-counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs into the traffic summary and exit")
+    ap.add_argument("--pmc-command", default="", help="the profiled command, recorded in the summary")
     ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
                     help="how persistent workgroups find tasks: host-built lists or a ticket counter")
     args = ap.parse_args()
 
+    if args.summarize_pmc:
+        t = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration << 20,
+                          args.workload, args.pmc_command)
+        with open(traffic_path(args.workload), "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -134,6 +219,16 @@ def main():
     assert plan["n_tasks"] - n_nop == n_closed, "timed graph must hold every layer and the lm_head"
     ptrs = inp.step_ptrs()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        from synth import native
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            native.gpu_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: 3 x {args.copy_calibration} MiB")
 
     # Both paths must agree before anything is timed.
     g.mk_decode_step(stream, *ptrs)
@@ -169,13 +264,15 @@ def main():
     achieved = bytes_step / (ms / 1e3) / 1e9
     log(f"persistent: {ms:.4f} ms/step, {tok_s:.1f} tok/s, {achieved:.0f} GB/s")
 
-    other = "dynamic" if args.schedule == "static" else "static"
-    g.mk_set_schedule(modes[other])
-    t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
-    assert g.mk_status() == 0
-    g.mk_set_schedule(modes[args.schedule])
-    alt = {"schedule": other, "ms_per_step": t_alt / args.steps}
-    log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
+    alt = None
+    if not args.no_alt_schedule:
+        other = "dynamic" if args.schedule == "static" else "static"
+        g.mk_set_schedule(modes[other])
+        t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
+        assert g.mk_status() == 0
+        g.mk_set_schedule(modes[args.schedule])
+        alt = {"schedule": other, "ms_per_step": t_alt / args.steps}
+        log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
 
     per_op = None
     if not args.no_per_op:
@@ -195,6 +292,8 @@ def main():
         g.mk_set_trace(None)
         np.save(args.trace_out, tr.cpu().numpy().reshape(-1, 8))
         np.save(args.trace_out.replace(".npy", "_tasks.npy"), tasks)
+
+    traffic = measured_traffic(w.name) if not args.kv_chunk else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -224,7 +323,7 @@ def main():
                        "p90": float(np.percentile(per, 90))},
         "bytes_per_step": bytes_step,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "per_op_baseline": per_op,
         "other_schedule": alt,
         "cpu_baseline": cpu,

@@ -203,9 +203,12 @@ int mk_set_wait_limit(mk_graph* g, uint64_t ticks);
 
 /* Trace mode: when `trace_dev` is non-NULL (device pointer, n_tasks * 8 uint64), the
  * next mk_decode_step calls record per task {XCC_ID << 32 | HW_ID register, start
- * time, ready time (dependency wait over), body end time, release end time, 0, 0, 0},
- * times in ticks of the constant 100 MHz clock.  NULL turns it off.  The pointer must
- * stay valid while steps that use it run. */
+ * time, ready time (dependency wait over), body end time, release end time, mark 0,
+ * mark 1, mark 2}, times in ticks of the constant 100 MHz clock.  Marks are points
+ * inside a body (0 where a body sets none): GEMV -- input staged, last row reduced;
+ * ATTENTION_PARTIAL -- chunk folded, partials merged; ATTENTION_COMBINE -- weights
+ * computed.  NOP joins run no body and record nothing.  NULL turns it off.  The
+ * pointer must stay valid while steps that use it run. */
 int mk_set_trace(mk_graph* g, uint64_t* trace_dev);
 
 /* Number of workgroups the persistent kernel is launched with (one per CU). */

@@ -82,3 +82,19 @@ extern "C" int synth_gpu_fill_cache(void* dst, int dtype, uint64_t n_bg, uint64_
                        dst, dtype, n_bg, n_slots, head_dim, pitch, key, mean, scale);
     return (int)hipGetLastError();
 }
+
+// A plain device copy of n_bytes (a multiple of 16): every byte read once and
+// written once.  Profilers run it beside the decode step to calibrate their HBM byte
+// counters against a known traffic.
+__global__ void copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, uint64_t n) {
+    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride) dst[j] = src[j];
+}
+
+extern "C" int synth_gpu_copy(void* dst, const void* src, uint64_t n_bytes, void* stream) {
+    if (n_bytes % 16 != 0) return (int)hipErrorInvalidValue;
+    if (n_bytes == 0) return 0;
+    hipLaunchKernelGGL(copy16_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                       (uint4*)dst, n_bytes / 16);
+    return (int)hipGetLastError();
+}

@@ -64,6 +64,8 @@ def gpu_lib():
         lib.synth_gpu_fill_flat.argtypes = [vp, ctypes.c_int, u64, u64, u64, u64, dbl, dbl, vp]
         lib.synth_gpu_fill_flat.restype = ctypes.c_int
         lib.synth_gpu_fill_cache.argtypes = [vp, ctypes.c_int, u64, u64, u64, u64, u64, u64, dbl, dbl, vp]
+        lib.synth_gpu_copy.argtypes = [vp, vp, u64, vp]
+        lib.synth_gpu_copy.restype = ctypes.c_int
         lib.synth_gpu_fill_cache.restype = ctypes.c_int
         _gpu = lib
     return _gpu
@@ -111,3 +113,10 @@ def gpu_fill_cache(ptr: int, n_bg: int, n_slots: int, head_dim: int, seed: int, 
                                         seed, tid, mean, gen.scale_for(std), stream)
     if rc != 0:
         raise RuntimeError(f"synth_gpu_fill_cache failed: hip error {rc}")
+
+
+def gpu_copy(dst_ptr: int, src_ptr: int, n_bytes: int, stream: int = 0) -> None:
+    """Plain 16-byte device copy (byte-counter calibration)."""
+    rc = gpu_lib().synth_gpu_copy(dst_ptr, src_ptr, n_bytes, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_gpu_copy failed ({rc})")

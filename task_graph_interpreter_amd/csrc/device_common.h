@@ -39,6 +39,7 @@ struct Smem {
   float red[kRedFloats];          // reductions
   alignas(16) mk_task_t desc[2];  // current / next descriptor (double-buffered)
   uint64_t t_ready;               // trace: when the dependency wait ended
+  uint64_t t_mark[3];             // trace: optional points inside a task body
   uint32_t ticket[2];
   uint32_t flag;
 };
@@ -156,15 +157,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// The value held by lane (this lane ^ OFF), OFF a power of two below 64, without an
+// LDS round trip where gfx950 has a VALU form: DPP quad_perm for 1 and 2, DPP
+// row_ror:8 for 8, v_permlane16_swap / v_permlane32_swap for 16 and 32 (each swap
+// hands back both halves; the lane keeps its partner's); ds_swizzle (xor mode)
+// for 4.
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (OFF == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));
+  else if constexpr (OFF == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
+  else if constexpr (OFF == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle((int)u, (4 << 10) | 0x1F));
+  else if constexpr (OFF == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false));
+  else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(OFF == 32, "lane_xor offset");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+__device__ __forceinline__ float wave_sum(float v) {
+  v += lane_xor<32>(v);
+  v += lane_xor<16>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<1>(v);
   return v;
 }
 
@@ -203,8 +224,8 @@ __device__ __forceinline__ float group_allsum(float v) {
   if constexpr (W >= 4) v = dpp_swap_add<0x4E>(v);
   if constexpr (W >= 8) v = dpp_swap_add<0x141>(v);
   if constexpr (W >= 16) v = dpp_swap_add<0x140>(v);
-  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  if constexpr (W >= 32) v += lane_xor<16>(v);
+  if constexpr (W >= 64) v += lane_xor<32>(v);
   return v;
 }
 __device__ __forceinline__ float group_allsum(float v, int width) {
@@ -218,6 +239,11 @@ __device__ __forceinline__ float group_allsum(float v, int width) {
 }
 
 __device__ __forceinline__ uint64_t clock100() { return wall_clock64(); }
+
+// Trace mode: thread 0 records a point inside a task body (trace words 5..7).
+__device__ __forceinline__ void trace_mark(const LaunchArgs& a, Smem& sm, int i) {
+  if (a.trace != nullptr && threadIdx.x == 0) sm.t_mark[i] = clock100();
+}
 
 __device__ __forceinline__ void raise_status(const LaunchArgs& a, uint32_t code) {
   uint32_t expected = 0u;

@@ -129,7 +129,10 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
     uint64_t t_claim = 0;
     uint32_t nt = 0;
     if (threadIdx.x == 0) {
-      if (trace) t_claim = clock100();
+      if (trace) {
+        t_claim = clock100();
+        sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
+      }
       nt = next_task(a, pos, end);
     }
     run_task_spec<S>(a, d, t, sm);
@@ -150,6 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
       stg<uint64_t>(a.trace, 8ull * t + 2, sm.t_ready);
       stg<uint64_t>(a.trace, 8ull * t + 3, t_end);
       stg<uint64_t>(a.trace, 8ull * t + 4, t_rel);
+      for (int i = 0; i < 3; ++i) stg<uint64_t>(a.trace, 8ull * t + 5 + i, sm.t_mark[i]);
     }
   }
 }

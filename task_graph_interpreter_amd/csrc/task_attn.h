@@ -105,6 +105,21 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2
   m = M;
 }
 
+// Log-sum-exp merge of every lane's running state with that of lane ^ OFF.
+template <int OFF, int HM, int VEC>
+__device__ __forceinline__ void merge_groups(float (&m)[HM], float (&l)[HM], float (&o)[HM][8], int hc) {
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    if (h < hc) {
+      const float m2 = lane_xor<OFF>(m[h]), l2 = lane_xor<OFF>(l[h]);
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o2[e] = lane_xor<OFF>(o[h][e]);
+      lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
+    }
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
   if (BF16) {
@@ -252,16 +267,26 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
     const size_t rn = head_off + (size_t)pos * rowq + dl;
     fold(ld_dev_u4(kc, rn), ld_dev_u4(vc, rn), wave == 0 && kl == 0);
   }
+  trace_mark(a, sm, 0);
   // Merge the lane groups of the wavefront (offsets lpk .. 32).
-  for (int off = lpk; off < 64; off <<= 1) {
+  if constexpr (LPK > 0) {
+    if constexpr (LPK <= 1) merge_groups<1, HM, VEC>(m, l, o, hc);
+    if constexpr (LPK <= 2) merge_groups<2, HM, VEC>(m, l, o, hc);
+    if constexpr (LPK <= 4) merge_groups<4, HM, VEC>(m, l, o, hc);
+    if constexpr (LPK <= 8) merge_groups<8, HM, VEC>(m, l, o, hc);
+    if constexpr (LPK <= 16) merge_groups<16, HM, VEC>(m, l, o, hc);
+    if constexpr (LPK <= 32) merge_groups<32, HM, VEC>(m, l, o, hc);
+  } else {
+    for (int off = lpk; off < 64; off <<= 1) {
 #pragma unroll
-    for (int h = 0; h < HM; ++h) {
-      if (h < hc) {
-        const float m2 = __shfl_xor(m[h], off, 64), l2 = __shfl_xor(l[h], off, 64);
-        float o2[8];
+      for (int h = 0; h < HM; ++h) {
+        if (h < hc) {
+          const float m2 = __shfl_xor(m[h], off, 64), l2 = __shfl_xor(l[h], off, 64);
+          float o2[8];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(o[h][e], off, 64);
-        lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
+          for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(o[h][e], off, 64);
+          lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
+        }
       }
     }
   }
@@ -283,6 +308,7 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
     }
   }
   __syncthreads();
+  trace_mark(a, sm, 1);
   for (int e = threadIdx.x; e < hc * stride; e += kThreads) {
     const int h = e / stride, dd = e % stride;
     float M = -INFINITY;
@@ -365,6 +391,7 @@ __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_
     ml[2 * i] = m == -INFINITY ? 0.f : __expf(m - Mh[i % hc]);
   }
   __syncthreads();
+  trace_mark(a, sm, 0);
   // 4. O[h][dd] = sum_c w_c o_c[dd] / lam, eight chunks' loads in flight at a time.
   for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
     const int h = e / hd, dd = e % hd;

@@ -203,6 +203,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     if (b0 == 0 && !dep_wait(a, t, d.remaining_deps, sm)) return;
     float rs[BM];
     gemv_stage<BM>(x, aux, d.config_id != MK_GEMV_F32, norm, g.K, b0, nb, a.rms_eps, sm, rs);
+    if (b0 == 0) trace_mark(a, sm, 0);
     if (g.NQ > 0) {
       float park[BM];
 #pragma unroll
@@ -250,6 +251,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
             gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
         }
       }
+      if (b0 == 0) trace_mark(a, sm, 1);
       gemv_flush<BM>(g, park, ((g.NQ - 1) >> 6) << 6, nb, resid, (const float*)aux, y, N, b0);
     }
     if (b0 + bp < B) __syncthreads();  // LDS reused by the next batch block
