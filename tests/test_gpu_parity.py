@@ -147,6 +147,24 @@ def test_bad_position_reports_status_then_recovers():
     run.close()
 
 
+@pytest.mark.parametrize("bad", [-1, 1024])
+def test_bad_token_reports_status_then_recovers(bad):
+    # An out-of-range token id is clamped to row 0 for the gather (no out-of-bounds
+    # read) and reported through the status word; the next good step is bitwise equal.
+    w = workloads.tiny()
+    _say(f"tiny bad token {bad}")
+    run = MkRun(w)
+    good = run.step("persistent")
+    run.inp.set_step(np.array([bad], dtype=np.int32), w.positions())
+    run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
+    st = run.graph.mk_status()
+    assert st & 0xF0000000 == 0x30000000 and st & 0x0FFFFFFF == 0  # the MEMCPY is task 0
+    run.inp.set_step(w.tokens(), w.positions())
+    run.inp.refill_caches()
+    assert np.array_equal(run.step("persistent"), good)
+    run.close()
+
+
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
 def test_wait_timeout_drains_and_recovers(mode):
     # A 1-tick bound on every dependency wait: tasks whose producers are not done at
