@@ -25,7 +25,7 @@ template <bool WBF16_, bool KVBF16_, int BM_, int KBA_, int KBD_>
 struct Spec {
   static constexpr bool WBF16 = WBF16_;    // weights bf16 (else fp32)
   static constexpr bool KVBF16 = KVBF16_;  // KV cache bf16 (else fp32)
-  static constexpr int BM = BM_;           // batch rows per GEMV pass (1 or 8)
+  static constexpr int BM = BM_;           // batch rows per GEMV pass (1 or 8); 32: MFMA tiles
   static constexpr int KBA = KBA_;         // kblocks of K = hidden (0: generic)
   static constexpr int KBD = KBD_;         // kblocks of K = intermediate (0: generic)
 };
@@ -46,6 +46,10 @@ __device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d,
 
 template <class S>
 __device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  if constexpr (S::BM == 32) {  // batched tiles on the matrix cores (every GEMV of the graph)
+    gemv_mfma(a, d, t, sm);
+    return;
+  }
   constexpr int VEC = S::WBF16 ? 8 : 4;
   const int kb = (d.k / VEC + 63) >> 6;
   if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm);

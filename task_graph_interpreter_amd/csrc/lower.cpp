@@ -200,6 +200,8 @@ int validate_cfg(const mk_model_cfg* c) {
   for (int64_t K : Ks) {
     if ((K * wes) % 16) return set_error(MK_ERR_INVALID, "GEMV inner dims must be multiples of 16 bytes");
     if (K > 32768) return set_error(MK_ERR_INVALID, "GEMV inner dim above 32768 (LDS staging)");
+    if (c->gemv_config == MK_GEMV_BF16_MFMA && K % 256)
+      return set_error(MK_ERR_INVALID, "the MFMA GEMV needs every inner dim % 256 == 0 (chunks of 8 x 32)");
   }
   // The GEMV addresses a weight matrix with 32-bit byte offsets.
   const int64_t H = c->hidden;

@@ -8,6 +8,7 @@
 #include "device_common.h"
 #include "task_attn.h"
 #include "task_gemv.h"
+#include "task_gemv_mfma.h"
 
 namespace mk {
 

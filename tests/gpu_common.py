@@ -27,6 +27,26 @@ def check_close(gpu, ref, what, atol=ATOL, rtol=RTOL):
     return float(err.max())
 
 
+def check_tokens(gpu_logits, ref_logits, what="tokens"):
+    """Greedy tokens per row: equal to the oracle's, except where the oracle's own
+    top-1 logit and the logit of the GPU's pick differ by less than twice the row's
+    largest measured logit error (a tie within error: the GPU's pick must then be one of
+    the near-tied candidates).  Returns the rows that were ties within error."""
+    ties = []
+    for b, (g, r) in enumerate(zip(np.asarray(gpu_logits, np.float64), np.asarray(ref_logits, np.float64))):
+        tg, tr = int(np.argmax(g)), int(np.argmax(r))
+        if tg == tr:
+            continue
+        err = float(np.max(np.abs(g - r)))
+        margin = float(r[tr] - r[tg])
+        assert margin <= 2.0 * err, (f"{what}: row {b} picks {tg}, oracle {tr}; oracle margin {margin:.3e} "
+                                     f"exceeds twice the row's logit error {err:.3e}")
+        ties.append(b)
+    if ties:
+        print(f"[{what}] tie within error on rows {ties}", flush=True)
+    return ties
+
+
 class MkRun:
     """Inputs on the GPU + an uploaded graph for workload ``w``."""
 
