@@ -17,10 +17,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;  // 8 wave64s per workgroup, one workgroup per CU
 constexpr int kWaves = kThreads / 64;
-// LDS: x staging / attention merge.  Above half of the CU's 160 KB, so the persistent
-// kernel gets exactly one workgroup per CU (co-residency of the whole grid).
-constexpr int kSmemBytes = 128 * 1024;
+// LDS: x staging, GEMV weight prefetch, attention merge.  Most of the CU's 160 KB, so
+// the persistent kernel gets exactly one workgroup per CU (co-residency of the whole
+// grid).
+constexpr int kSmemBytes = 148 * 1024;
 constexpr int kRedFloats = 1024;  // reduction scratch
+
+// Arrival counters sit one per 128-byte line, so the atomics of a join's fan-out (one
+// wave incrementing up to 256 children) and the children's polls never share a line.
+constexpr uint32_t kArrivalStride = 32;
 
 // Buffer-table entry tags (top byte): 0 = absolute device pointer; otherwise an
 // offset into a per-step base passed at launch.
@@ -52,7 +57,7 @@ struct LaunchArgs {
   const uint32_t* order;      // static schedule: task lists grouped by workgroup
   const uint32_t* order_off;  // [grid + 1]; null = dynamic tickets
   const uint64_t* table;
-  uint32_t* arrivals;
+  uint32_t* arrivals;  // one counter per kArrivalStride words
   Ctrl* ctrl;
   uint64_t* trace;
   uint64_t rt[8];  // per-step bases indexed by tag
@@ -135,8 +140,11 @@ __device__ __forceinline__ f32x4 ld_dev_f4(const void* p, size_t i4) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// The buffer table is written by the host before the launch and only read here: a
+// scalar load through the constant address space (counted by lgkmcnt, so it never
+// makes a wave wait behind its own outstanding vector loads).
 __device__ __forceinline__ char* resolve(const LaunchArgs& a, uint32_t idx) {
-  const uint64_t e = ldg<uint64_t>(a.table, idx);
+  const uint64_t e = ((const __attribute__((address_space(4))) uint64_t*)a.table)[idx];
   const uint32_t tag = (uint32_t)(e >> kTagShift);
   // Compare chain instead of indexing a.rt with a run-time tag (an indexed kernel
   // argument would be copied to private memory).
@@ -268,7 +276,7 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
     return true;
   }
   if (threadIdx.x == 0) {
-    MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + t;
+    MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + (size_t)t * kArrivalStride;
     const uint32_t target = a.epoch * (uint32_t)indeg;
     uint32_t ok = 1;
     uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -310,7 +318,7 @@ __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t 
     if (i < n) {
       const uint32_t e = ldg<uint32_t>(a.edges, off + i);
       const uint32_t c = e & 0x7FFFFFFFu;
-      MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + c;
+      MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + (size_t)c * kArrivalStride;
       if (e >> 31) {
         const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t indeg = ldg<uint32_t>(a.tasks, (size_t)c * 16 + 2);  // remaining_deps
@@ -330,7 +338,7 @@ __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t 
       const uint32_t no = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 4));
       for (uint32_t j = lane; j < nd; j += 64) {
         const uint32_t cc = ldg<uint32_t>(a.edges, no + j) & 0x7FFFFFFFu;
-        __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + cc, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + (size_t)cc * kArrivalStride, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
       }
     }

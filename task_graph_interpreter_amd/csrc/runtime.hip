@@ -56,7 +56,8 @@ static const SpecEntry* select_spec(const mk_model_cfg& c) {
 }
 
 __global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) arrivals[i] = 0;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    arrivals[(size_t)i * kArrivalStride] = 0;
   if (blockIdx.x == 0 && threadIdx.x < sizeof(Ctrl) / 4) ((uint32_t*)ctrl)[threadIdx.x] = 0;
 }
 
@@ -277,7 +278,7 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   std::memcpy(blob.data() + off_order_off, S.offsets.data(), S.offsets.size() * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
   if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
-  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4)) != hipSuccess)
+  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4 * (size_t)mk::kArrivalStride)) != hipSuccess)
     return fail(hip_fail(e, "hipMalloc(arrivals)"));
   if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
   g->d_tasks = (mk_task_t*)(g->d_blob + off_tasks);

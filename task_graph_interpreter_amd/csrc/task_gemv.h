@@ -48,6 +48,19 @@ __device__ __forceinline__ u32x4 gemv_load(const GemvGeom& g, int q, int kb, int
   return __builtin_nontemporal_load((const MK_GLOBAL u32x4*)((const MK_GLOBAL char*)g.W + off));
 }
 
+// The same 16 bytes as gemv_load, copied straight into LDS at `dst` (+ 16 * lane):
+// a direct global-to-LDS load, so a prefetched row occupies no registers.
+__device__ __forceinline__ void gemv_load_lds(const GemvGeom& g, int q, int kb, int lane, char* dst) {
+  q = q < g.NQ ? q : g.NQ - 1;
+  const int j = g.silu ? (q >> 1) : q;
+  const int row = g.c0 + g.wave + kWaves * j + ((g.silu && (q & 1)) ? g.I : 0);
+  int chunk = kb * 64 + lane;
+  chunk = chunk < g.KC ? chunk : g.KC - 1;
+  const uint32_t off = ((uint32_t)row * (uint32_t)g.KC + (uint32_t)chunk) * 16u;
+  __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL char*)g.W + off),
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 template <int BM, bool BF16>
 __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int K, int chunk, bool valid, int nb,
                                              float acc[BM]) {
@@ -189,16 +202,36 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
   int bp = (kSmemBytes / 4) / g.K;
   bp = bp < BM ? bp : BM;
-  const int iters = (g.NQ + RPG - 1) / RPG;
 
   for (int b0 = 0; b0 < B; b0 += bp) {
     const int nb = (B - b0) < bp ? (B - b0) : bp;
+    // Static-input prefetch into LDS: the LDS left after the staged input holds the
+    // wave's first PF whole rows, loaded before the dependency wait (single-pass tiles
+    // of at most 64 rows per wave).  Those rows are consumed last, after the register
+    // ring has streamed the rest.
+    // The register ring's first rows are issued before the LDS rows: loads complete in
+    // issue order, so the ring never waits behind the prefetch.
+    constexpr int KBR = KBS * SEG;  // kblocks per row (compile-time path)
+    int PF = 0;
+    char* pfw = nullptr;
+    if (KBT > 0 && b0 == 0 && nb == B && g.NQ <= 64) {
+      const int xfl = (B * g.K + 3) & ~3;
+      const int per_wave = ((kSmemBytes - 4 * xfl) / kWaves) & ~1023;
+      PF = per_wave / (KBR * 1024);
+      PF = PF < g.NQ ? PF : g.NQ;
+      pfw = (char*)(sm.xs + xfl) + g.wave * per_wave;
+    }
     u32x4 buf[RPG][KBS];
-    if (KBT > 0 && g.NQ > 0) {
+    if (KBT > 0 && g.NQ > PF) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r)
 #pragma unroll
-        for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, r, kb, lane);
+        for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, PF + r, kb, lane);
+    }
+    if (KBT > 0) {
+      for (int q = 0; q < PF; ++q)
+#pragma unroll
+        for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(g, q, kb, lane, pfw + (q * KBR + kb) * 1024);
     }
     if (b0 == 0 && !dep_wait(a, t, d.remaining_deps, sm)) return;
     float rs[BM];
@@ -208,8 +241,9 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
       float park[BM];
 #pragma unroll
       for (int b = 0; b < BM; ++b) park[b] = 0.f;
-      for (int it = 0; it < iters; ++it) {
-        const int q0 = it * RPG;
+      const int iters_ring = (g.NQ - PF + RPG - 1) / RPG;
+      for (int it = 0; it < iters_ring; ++it) {
+        const int q0 = PF + it * RPG;
         // Short rows: the compiler may keep the staged input in registers across rows.
         // Long rows: an opaque offset keeps the LDS reads inside the loop instead of
         // pinning 8 registers per kblock.
@@ -249,6 +283,28 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
           }
           if ((q & 63) == 63 && q + 1 < g.NQ)  // more than 64 rows per wave: flush now
             gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
+        }
+      }
+      if (KBT > 0) {
+        // The LDS-resident rows (PF > 0 only when the wave has at most 64 rows, so the
+        // final flush covers them).
+        for (int q = 0; q < PF; ++q) {
+          float acc[BM];
+#pragma unroll
+          for (int b = 0; b < BM; ++b) acc[b] = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < KBR; ++kb) {
+            const u32x4 wv = *(const u32x4*)(pfw + (q * KBR + kb) * 1024 + 16 * lane);
+            const int chunk = kb * 64 + lane;
+            gemv_consume<BM, BF16>(wv, sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
+          }
+#pragma unroll
+          for (int b = 0; b < BM; ++b) {
+            if (b < nb) {
+              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(acc[b])), 63));
+              park[b] = (lane == (q & 63)) ? v * rs[b] : park[b];
+            }
+          }
         }
       }
       if (b0 == 0) trace_mark(a, sm, 1);
