@@ -171,13 +171,13 @@ def tiny() -> Workload:
 def llama1b() -> Workload:
     return Workload(name="1b_b1", n_layers=16, hidden=2048, n_q_heads=32, n_kv_heads=8, head_dim=64,
                     intermediate=8192, vocab=128256, batch=1, weight_dtype="bf16", kv_dtype="bf16",
-                    gemv_tiles=256, kv_chunk=256, kv_len=(1024,), kv_capacity=1024, gemv_config=1)
+                    gemv_tiles=256, kv_chunk=128, kv_len=(1024,), kv_capacity=1024, gemv_config=1)
 
 
 def llama8b() -> Workload:
     return Workload(name="8b_b1", n_layers=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
                     intermediate=14336, vocab=128256, batch=1, weight_dtype="bf16", kv_dtype="bf16",
-                    gemv_tiles=256, kv_chunk=256, kv_len=(2048,), kv_capacity=2048, gemv_config=1)
+                    gemv_tiles=256, kv_chunk=128, kv_len=(2048,), kv_capacity=2048, gemv_config=1)
 
 
 def llama8b_ragged(seed: int = 0) -> Workload:

@@ -26,6 +26,10 @@ constexpr int kRedFloats = 1024;  // reduction scratch
 // Arrival counters sit one per 128-byte line, so the atomics of a join's fan-out (one
 // wave incrementing up to 256 children) and the children's polls never share a line.
 constexpr uint32_t kArrivalStride = 32;
+// Word 3 of a raw (stride 0, untyped) buffer resource on gfx950, and the cache-policy
+// operand of a buffer load that streams (non-temporal).
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;
 
 // Buffer-table entry tags (top byte): 0 = absolute device pointer; otherwise an
 // offset into a per-step base passed at launch.

@@ -12,9 +12,10 @@
 //  * one loop iteration consumes RPG whole rows held in a ring of RPG * KBT registers
 //    and refills each slot with the same kblock of the row RPG ahead, so RPG * KBT
 //    16-byte loads per lane stay in flight.  The loop body is straight-line code:
-//    loads are unconditional (rows past the wave's last one re-read that row; the
-//    results are discarded), so the compiler's wait counts stay exact instead of
-//    draining the ring at every branch;
+//    loads are unconditional, so the compiler's wait counts stay exact instead of
+//    draining the ring at every branch.  Weights are read with buffer loads; a slot
+//    refilled past the wave's last row gets an offset beyond the buffer's range, which
+//    the hardware answers with zeros and no memory access (its result is discarded);
 //  * the ring's first fill is issued before the dependency wait: weights are static,
 //    so the tile's first bytes arrive while its producers are still finishing;
 //  * the input rows are staged once per task in LDS (fp32, x * gamma);
@@ -27,8 +28,14 @@
 
 namespace mk {
 
+// Range of the weight buffer resource: every offset of a matrix (< 4 GiB, checked when
+// lowering, rows a multiple of 16 bytes) is below it; kPastEnd is not.
+constexpr uint32_t kWeightRange = 0xFFFFFFF0u;
+constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+
 struct GemvGeom {
   const char* W;
+  __amdgpu_buffer_rsrc_t wr;  // raw buffer over W (stride 0, range kWeightRange)
   int K, KC;      // inner dim, 16-byte chunks per row
   int c0, I;      // first output column, up-row offset (SILU_MUL)
   int nout, NQ;   // outputs of this wave, logical rows of this wave
@@ -37,15 +44,14 @@ struct GemvGeom {
 };
 
 __device__ __forceinline__ u32x4 gemv_load(const GemvGeom& g, int q, int kb, int lane) {
-  q = q < g.NQ ? q : g.NQ - 1;  // past the last row: re-read it (discarded)
+  const bool past = q >= g.NQ;  // past the wave's last row: out of range, reads nothing
   const int j = g.silu ? (q >> 1) : q;
   const int row = g.c0 + g.wave + kWaves * j + ((g.silu && (q & 1)) ? g.I : 0);
   int chunk = kb * 64 + lane;
   chunk = chunk < g.KC ? chunk : g.KC - 1;  // partial last kblock: masked when consumed
-  // 32-bit byte offset from the (scalar) matrix base: every weight matrix is < 4 GiB
-  // (checked when lowering), so the load uses a scalar base + 32-bit vector offset.
+  // 32-bit byte offset into the matrix (every weight matrix is < 4 GiB).
   const uint32_t off = ((uint32_t)row * (uint32_t)g.KC + (uint32_t)chunk) * 16u;
-  return __builtin_nontemporal_load((const MK_GLOBAL u32x4*)((const MK_GLOBAL char*)g.W + off));
+  return __builtin_amdgcn_raw_buffer_load_b128(g.wr, past ? kPastEnd : off, 0, kCachePolicyNT);
 }
 
 // The same 16 bytes as gemv_load, copied straight into LDS at `dst` (+ 16 * lane):
@@ -185,6 +191,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
   GemvGeom g;
   g.wave = wave_id();
   g.W = resolve(a, d.in_buf[1]);
+  g.wr = __builtin_amdgcn_make_buffer_rsrc((void*)g.W, (short)0, (int)kWeightRange, kRawBufferWord3);
   g.K = d.k;
   g.KC = d.k / VEC;
   g.c0 = (int)d.reserved[0];
