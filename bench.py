@@ -170,6 +170,7 @@ def main():
     ap.add_argument("--no-alt-schedule", action="store_true", help="skip timing the other schedule mode")
     ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
+    ap.add_argument("--gemv-tiles", type=int, default=0, help="override the workload's GEMV tiles per matmul")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (byte-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -203,6 +204,8 @@ def main():
     w = workloads.get(args.workload)
     if args.kv_chunk:
         w = w.replace(kv_chunk=args.kv_chunk)
+    if args.gemv_tiles:
+        w = w.replace(gemv_tiles=args.gemv_tiles)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
     inp = DeviceInputs(w)
@@ -293,7 +296,7 @@ def main():
         np.save(args.trace_out, tr.cpu().numpy().reshape(-1, 8))
         np.save(args.trace_out.replace(".npy", "_tasks.npy"), tasks)
 
-    traffic = measured_traffic(w.name) if not args.kv_chunk else None
+    traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles) else None
 
     cpu = None
     if not args.no_cpu_baseline:

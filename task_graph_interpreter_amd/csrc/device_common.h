@@ -46,11 +46,12 @@ struct Ctrl {
 struct Smem {
   float xs[kSmemBytes / 4];       // staged activations / attention merge
   float red[kRedFloats];          // reductions
-  alignas(16) mk_task_t desc[2];  // current / next descriptor (double-buffered)
+  alignas(16) mk_task_t desc[3];  // current, next and next-but-one descriptors (rotating)
   uint64_t t_ready;               // trace: when the dependency wait ended
   uint64_t t_mark[3];             // trace: optional points inside a task body
-  uint32_t ticket[2];
+  uint32_t ticket[3];
   uint32_t flag;
+  uint32_t stop;  // set when a task raised an error status: end after the current task
 };
 
 struct LaunchArgs {

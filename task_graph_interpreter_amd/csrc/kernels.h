@@ -31,42 +31,83 @@ struct Spec {
 };
 
 // A row of KB kblocks -> (kblocks per segment, segments, rows in flight): 8 or 14
-// loads of 16 bytes in flight per lane.
+// loads of 16 bytes in flight per lane.  Other row lengths take the generic path.
+constexpr bool kb_compiled(int KB) { return KB == 1 || KB == 2 || KB == 4 || KB == 8 || KB == 16 || KB == 28; }
+
 template <int BM, bool BF16, int KB>
-__device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
-  if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm);
-  else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm);
-  else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm);
-  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm);
-  else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm);
-  else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm);
-  else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm);
-  else gemv_run<BM, BF16, 0, 1, 1>(a, d, t, sm);
+__device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
+  if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm, pre);
+  else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm, pre);
+  else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm, pre);
+  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm, pre);
+  else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm, pre);
+  else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm, pre);
+  else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm, pre);
+  else gemv_run<BM, BF16, 0, 1, 1>(a, d, t, sm, false);
 }
 
 template <class S>
-__device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+__device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
   if constexpr (S::BM == 32) {  // batched tiles on the matrix cores (every GEMV of the graph)
     gemv_mfma(a, d, t, sm);
     return;
   }
   constexpr int VEC = S::WBF16 ? 8 : 4;
   const int kb = (d.k / VEC + 63) >> 6;
-  if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm);
-  else if (S::KBD > 0 && S::KBD != S::KBA && kb == S::KBD) gemv_kb<S::BM, S::WBF16, S::KBD>(a, d, t, sm);
-  else gemv_run<S::BM, S::WBF16, 0, 1, 1>(a, d, t, sm);
+  if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm, pre);
+  else if (S::KBD > 0 && S::KBD != S::KBA && kb == S::KBD) gemv_kb<S::BM, S::WBF16, S::KBD>(a, d, t, sm, pre);
+  else gemv_run<S::BM, S::WBF16, 0, 1, 1>(a, d, t, sm, false);
 }
 
+// Issue the LDS prefetch of the workgroup's next task dn (a GEMV tile on the
+// compile-time streaming path) while the current task, which uses at most lds_used
+// bytes at the start of the LDS, is still waiting or running.  Returns whether the
+// prefetch was issued (the tile then skips its own).
 template <class S>
-__device__ __forceinline__ void run_task_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+__device__ __forceinline__ bool gemv_spec_prefetch(const LaunchArgs& a, const mk_task_t& dn, int lds_used, Smem& sm) {
+  if constexpr (S::BM == 32) {
+    return false;
+  } else {
+    if (dn.op_id != MK_OP_GEMV) return false;
+    constexpr int VEC = S::WBF16 ? 8 : 4;
+    const int kb = (dn.k / VEC + 63) >> 6;
+    if constexpr (S::KBA > 0 && kb_compiled(S::KBA))
+      if (kb == S::KBA) return gemv_prefetch_ahead<S::BM, S::WBF16, S::KBA>(a, dn, lds_used, sm);
+    if constexpr (S::KBD > 0 && S::KBD != S::KBA && kb_compiled(S::KBD))
+      if (kb == S::KBD) return gemv_prefetch_ahead<S::BM, S::WBF16, S::KBD>(a, dn, lds_used, sm);
+    return false;
+  }
+}
+
+// Bytes at the start of the LDS used by a task under which the next GEMV tile's LDS
+// prefetch is issued early (-1: none).  Only the combine qualifies: it waits for
+// every partial of its group and touches no LDS, while APPEND and the partials sit on
+// the critical path, where a bulk prefetch issued first would delay their own loads
+// (a wave's loads complete in issue order).
+__device__ __forceinline__ int prefetch_host_lds_bytes(const mk_task_t& d) {
+  return d.op_id == MK_OP_ATTENTION_COMBINE ? 0 : -1;
+}
+
+// Run task t.  pre: its LDS prefetch was issued by the previous task.  dn (may be
+// null): the workgroup's next task; a combine issues dn's LDS prefetch first when dn
+// is a GEMV tile on the streaming path.  Returns whether that prefetch was issued.
+template <class S>
+__device__ __forceinline__ bool run_task_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre,
+                                              const mk_task_t* dn) {
+  bool ahead = false;
+  if (dn != nullptr) {
+    const int used = prefetch_host_lds_bytes(d);
+    if (used >= 0) ahead = gemv_spec_prefetch<S>(a, *dn, used, sm);
+  }
   switch (d.op_id) {
-    case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm); break;
+    case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm, pre); break;
     case MK_OP_ATTENTION_APPEND: task_append(a, d, t, sm); break;
     case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
     case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
     default: break;  // NOP joins never run as tasks: their last parent fires them
   }
+  return ahead;
 }
 
 __device__ __forceinline__ uint32_t claim_ticket(const LaunchArgs& a) {
@@ -104,12 +145,17 @@ __device__ __forceinline__ uint32_t next_task(const LaunchArgs& a, uint32_t& pos
   }
 }
 
-// The persistent interpreter.  The next task is fetched one task ahead (the claim's
-// round trip, or the list read, and the descriptor fetch overlap the current task);
-// descriptors and task ids are double-buffered in LDS, which is safe because every
-// iteration ends in a workgroup barrier.  In dynamic mode each workgroup makes exactly
-// one failing claim per step, so the ticket counter advances by n_tasks + grid per
-// step and never needs a reset.  Trace mode (a.trace != null) records timestamps.
+// The persistent interpreter.  Tasks are fetched two ahead: while task i runs, the
+// descriptors of tasks i and i + 1 are in LDS and the id of task i + 2 is being
+// fetched (the claim's round trip, or the list read, and the descriptor fetch overlap
+// the current task), and an attention task can start the next GEMV tile's LDS
+// prefetch.  Descriptors and ids rotate through three LDS slots, which is safe because
+// every iteration ends in a workgroup barrier and slot i + 2 is written only at the
+// end of iteration i.  In dynamic mode each workgroup makes exactly one failing claim
+// per step, so the ticket counter advances by n_tasks + grid per step and never needs
+// a reset; a workgroup holding two claimed tasks runs them in claim order, so the
+// lowest unfinished task is always running.  Trace mode (a.trace != null) records
+// timestamps.
 template <class S>
 __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) {
   __shared__ Smem sm;
@@ -122,30 +168,39 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
     }
     uint32_t t0 = next_task(a, pos, end);
     if (read_status(a) != 0) t0 = 0xFFFFFFFFu;
+    const uint32_t t1 = t0 < a.n_tasks ? next_task(a, pos, end) : 0xFFFFFFFFu;
     sm.ticket[0] = t0;
+    sm.ticket[1] = t1;
+    sm.stop = 0;
     if (t0 < a.n_tasks) stage_desc(a, t0, sm, 0);
+    if (t1 < a.n_tasks) stage_desc(a, t1, sm, 1);
   }
   __syncthreads();
-  for (int it = 0;; it ^= 1) {
-    const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket[it]);
-    if (t >= a.n_tasks) break;
-    const mk_task_t d = read_desc(sm, it);
+  bool pre = false;  // this task's LDS prefetch was issued by the previous task
+  for (int s = 0;; s = s == 2 ? 0 : s + 1) {
+    const int s1 = s == 2 ? 0 : s + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket[s]);
+    if (t >= a.n_tasks || __builtin_amdgcn_readfirstlane(sm.stop) != 0) break;
+    const mk_task_t d = read_desc(sm, s);
+    const uint32_t tn = __builtin_amdgcn_readfirstlane(sm.ticket[s1]);
+    mk_task_t dn;
+    if (tn < a.n_tasks) dn = read_desc(sm, s1);
     uint64_t t_claim = 0;
-    uint32_t nt = 0;
+    uint32_t nn = 0xFFFFFFFFu;
     if (threadIdx.x == 0) {
       if (trace) {
         t_claim = clock100();
         sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
       }
-      nt = next_task(a, pos, end);
+      if (tn < a.n_tasks) nn = next_task(a, pos, end);
     }
-    run_task_spec<S>(a, d, t, sm);
+    pre = run_task_spec<S>(a, d, t, sm, pre, tn < a.n_tasks ? &dn : nullptr);
     uint64_t t_end = 0;
     if (threadIdx.x == 0) {
       if (trace) t_end = clock100();
-      if (read_status(a) != 0) nt = 0xFFFFFFFFu;
-      sm.ticket[it ^ 1] = nt;
-      if (nt < a.n_tasks) stage_desc(a, nt, sm, it ^ 1);
+      if (read_status(a) != 0) sm.stop = 1;
+      sm.ticket[s2] = nn;
+      if (nn < a.n_tasks) stage_desc(a, nn, sm, s2);
     }
     release_dependents(a, d);
     if (trace && threadIdx.x == 0) {
@@ -172,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
   __syncthreads();
   mk_task_t d = read_desc(sm, 0);
   d.remaining_deps = 0;
-  run_task_spec<S>(a, d, t, sm);
+  run_task_spec<S>(a, d, t, sm, false, nullptr);
 }
 
 struct KernelSet {

@@ -209,6 +209,10 @@ int validate_cfg(const mk_model_cfg* c) {
                              H * (int64_t)c->intermediate, (int64_t)c->vocab * H};
   for (int64_t e : wbytes)
     if (e * wes >= (1ll << 32)) return set_error(MK_ERR_INVALID, "a weight matrix is 4 GiB or larger");
+  // The attention partial addresses one (sequence, KV head)'s cache rows with 32-bit
+  // byte offsets.
+  if ((int64_t)c->kv_capacity * c->head_dim * kes >= (1ll << 32))
+    return set_error(MK_ERR_INVALID, "one KV head's cache rows are 4 GiB or larger");
   const int64_t lpk = c->head_dim * kes / 16;
   if ((c->head_dim * kes) % 16 || lpk < 1 || lpk > 64 || (lpk & (lpk - 1)))
     return set_error(MK_ERR_INVALID, "head_dim * cache element size must be 16 * 2^j bytes, at most 1 KB");

@@ -165,10 +165,20 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   const int jbase = wave * kpw + kl;  // this lane group's row in round 0
   const int rounds = (n + kpr - 1) / kpr;
   const bool first = hg == 0;
-  // Rows past the chunk's end are clamped to its last row (loaded, then masked), so
-  // every load below is unconditional within a wave-uniform branch.
-  const int jmax = n > 0 ? n - 1 : 0;
-  auto row_idx = [&](int j) { return head_off + (size_t)(lo + (j < jmax ? j : jmax)) * rowq + dl; };
+  // K and V of this (sequence, KV head) are read through raw buffer resources over
+  // the head's cache rows.  A row past the chunk's end gets an out-of-range offset:
+  // the load returns zeros without touching memory and the row is masked when
+  // folded, so every load below is unconditional within a wave-uniform branch.
+  const uint32_t head_bytes = (uint32_t)cap * (uint32_t)rowq * 16u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kc + head_off * 16), (short)0, (int)head_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vc + head_off * 16), (short)0, (int)head_bytes, kRawBufferWord3);
+  auto row_off = [&](int j) -> uint32_t {
+    return j < n ? ((uint32_t)(lo + j) * (uint32_t)rowq + (uint32_t)dl) * 16u : 0xFFFFFFF0u;
+  };
+  auto ldk = [&](int j) { return __builtin_amdgcn_raw_buffer_load_b128(krs, row_off(j), 0, 0); };
+  auto ldv = [&](int j) { return __builtin_amdgcn_raw_buffer_load_b128(vrs, row_off(j), 0, 0); };
 
   // Rows of earlier steps never change during the step: the first R rounds are
   // loaded before the dependency wait.  The new token's row is loaded too but masked
@@ -177,8 +187,8 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   if (rounds > 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      kr[r] = ldg<u32x4>(kc, row_idx(jbase + r * kpr));
-      vr[r] = ldg<u32x4>(vc, row_idx(jbase + r * kpr));
+      kr[r] = ldk(jbase + r * kpr);
+      vr[r] = ldv(jbase + r * kpr);
     }
   }
   if (first) {
@@ -203,6 +213,16 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
         q[h][4] = q[h][5] = q[h][6] = q[h][7] = 0.f;
       }
     }
+  }
+  // The new token's row, written by this step's APPEND: wave 0 issues its
+  // device-scope loads together with the query's, and its lane group 0 folds the row
+  // in after the loop.
+  const bool has_new = jnew >= 0 && jnew < n;
+  u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
+  if (has_new && wave == 0) {
+    const size_t rn = head_off + (size_t)pos * rowq + dl;
+    knew = ld_dev_u4(kc, rn);
+    vnew = ld_dev_u4(vc, rn);
   }
   float m[HM], l[HM], o[HM][8];
 #pragma unroll
@@ -238,35 +258,36 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
     }
   };
   // Batches of R rounds, double-buffered: the next batch's loads are issued before
-  // the current batch is folded.  All loads are unconditional (clamped rows; the
-  // last batch's look-ahead re-reads the chunk's last row), so the compiler can keep
-  // 2R rounds in flight with counted waits.
+  // the current batch is folded.  Within a batch every load is unconditional (rows
+  // past the chunk are out of range and read nothing), so the compiler keeps 2R rounds
+  // in flight with counted waits.  The last batch issues no look-ahead: a load still
+  // in flight would hold up the workgroup barrier below by a memory round trip.
   const int nbatch = (rounds + R - 1) / R;
   for (int bt = 0; bt < nbatch; ++bt) {
+    const bool more = bt + 1 < nbatch;
     u32x4 kn[R], vn[R];
-    const int jn = jbase + (bt + 1) * R * kpr;
+    if (more) {
+      const int jn = jbase + (bt + 1) * R * kpr;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      kn[r] = ldg<u32x4>(kc, row_idx(jn + r * kpr));
-      vn[r] = ldg<u32x4>(vc, row_idx(jn + r * kpr));
+      for (int r = 0; r < R; ++r) {
+        kn[r] = ldk(jn + r * kpr);
+        vn[r] = ldv(jn + r * kpr);
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int j = jbase + (bt * R + r) * kpr;
       fold(kr[r], vr[r], j < n && j != jnew);
     }
+    if (more) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      kr[r] = kn[r];
-      vr[r] = vn[r];
+      for (int r = 0; r < R; ++r) {
+        kr[r] = kn[r];
+        vr[r] = vn[r];
+      }
     }
   }
-  // The new token's row, written by this step's APPEND: device-scope loads after the
-  // wait; lane group 0 of wave 0 folds it in.
-  if (jnew >= 0 && jnew < n) {
-    const size_t rn = head_off + (size_t)pos * rowq + dl;
-    fold(ld_dev_u4(kc, rn), ld_dev_u4(vc, rn), wave == 0 && kl == 0);
-  }
+  if (has_new && wave == 0) fold(knew, vnew, kl == 0);
   trace_mark(a, sm, 0);
   // Merge the lane groups of the wavefront (offsets lpk .. 32).
   if constexpr (LPK > 0) {
@@ -290,19 +311,21 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
       }
     }
   }
-  // Merge the wavefronts through LDS: [wave][head][hd + 2].
-  float* part = sm.xs;
-  if (!first) __syncthreads();  // the previous pass may still read `part`
+  // Merge the wavefronts through LDS: o in [wave][head][hd] at the start of the
+  // staging area, (m, l) in [wave][head][2] in the reduction area.
+  float* po = sm.xs;
+  float* pml = sm.red;
+  if (!first) __syncthreads();  // the previous pass may still read po / pml
   if (kl == 0) {
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
       if (h < hc) {
-        float* pw = part + ((size_t)wave * HM + h) * stride;
+        float* pw = po + ((size_t)wave * HM + h) * hd;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) pw[dl * VEC + e] = o[h][e];
         if (dl == 0) {
-          pw[hd] = m[h];
-          pw[hd + 1] = l[h];
+          pml[(wave * HM + h) * 2] = m[h];
+          pml[(wave * HM + h) * 2 + 1] = l[h];
         }
       }
     }
@@ -312,13 +335,13 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   for (int e = threadIdx.x; e < hc * stride; e += kThreads) {
     const int h = e / stride, dd = e % stride;
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, part[((size_t)w * HM + h) * stride + hd]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pml[(w * HM + h) * 2]);
     float acc = 0.f;
     for (int w = 0; w < kWaves; ++w) {
-      const float* pw = part + ((size_t)w * HM + h) * stride;
-      const float al = (pw[hd] == -INFINITY) ? 0.f : __expf(pw[hd] - M);
-      if (dd < hd) acc = fmaf(pw[dd], al, acc);
-      else if (dd == hd + 1) acc = fmaf(pw[hd + 1], al, acc);
+      const float mw = pml[(w * HM + h) * 2];
+      const float al = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+      if (dd < hd) acc = fmaf(po[((size_t)w * HM + h) * hd + dd], al, acc);
+      else if (dd == hd + 1) acc = fmaf(pml[(w * HM + h) * 2 + 1], al, acc);
     }
     st_dev<float>(out, out0 + h * stride + dd, (dd == hd) ? M : acc);
   }
@@ -353,6 +376,10 @@ __device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_ta
 // ---------------------------------------------------------------------------------
 // ATTENTION_COMBINE (OpId 9 of the same table): per head,
 // M = max_c m_c, w_c = e^(m_c - M), O = sum_c w_c o_c / sum_c w_c l_c.
+// One output element per thread.  The thread loads its o values and its head's
+// (m, l) for a block of chunks at once (one memory round trip per block of 16
+// chunks) and folds each block into a running (M, lam, O) with the same log-sum-exp
+// rule.  No LDS is used, so the workgroup's next GEMV tile can prefetch into it.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc = (int)d.reserved[2];
@@ -360,54 +387,39 @@ __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_
   const float* part = (const float*)resolve(a, d.in_buf[0]);
   float* att = (float*)resolve(a, d.out_buf);
   if (!dep_wait(a, t, d.remaining_deps, sm)) return;
-  const int Hq = a.n_q_heads, stride = hd + 2, np = nch * hc;
-  // Slot (chunk c, head h) of this group is partials[(base + c) * hc + h].
-  // 1. Every (m, l) into LDS: [np][2].
-  float* ml = sm.xs;
-  for (int i = threadIdx.x; i < np; i += kThreads) {
-    const size_t s = ((size_t)base * hc + i) * stride + hd;
-    ml[2 * i] = ld_dev<float>(part, s);
-    ml[2 * i + 1] = ld_dev<float>(part, s + 1);
-  }
-  __syncthreads();
-  // 2. Per head: M = max_c m_c and lam = sum_c e^(m_c - M) l_c.
-  float* Mh = sm.red;  // [hc] max, then [hc] lam
-  if (threadIdx.x < hc) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * (c * hc + h)]);
-    float lam = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float m = ml[2 * (c * hc + h)];
-      lam = fmaf(m == -INFINITY ? 0.f : __expf(m - M), ml[2 * (c * hc + h) + 1], lam);
-    }
-    Mh[h] = M;
-    Mh[hc + h] = lam;
-  }
-  __syncthreads();
-  // 3. Weights w_c = e^(m_c - M) in place of m.
-  for (int i = threadIdx.x; i < np; i += kThreads) {
-    const float m = ml[2 * i];
-    ml[2 * i] = m == -INFINITY ? 0.f : __expf(m - Mh[i % hc]);
-  }
-  __syncthreads();
-  trace_mark(a, sm, 0);
-  // 4. O[h][dd] = sum_c w_c o_c[dd] / lam, eight chunks' loads in flight at a time.
+  const int Hq = a.n_q_heads, stride = hd + 2;
+  constexpr int CB = 16;
   for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
     const int h = e / hd, dd = e % hd;
-    float o = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 8) {
-      float v[8];
+    float M = -INFINITY, lam = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += CB) {
+      float mv[CB], lv[CB], ov[CB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u < nch ? c0 + u : nch - 1;
-        v[u] = ld_dev<float>(part, ((size_t)(base + c) * hc + h) * stride + dd);
+      for (int u = 0; u < CB; ++u) {
+        const int c = c0 + u < nch ? c0 + u : nch - 1;  // past the last chunk: masked below
+        const size_t s0 = ((size_t)(base + c) * hc + h) * stride;
+        ov[u] = ld_dev<float>(part, s0 + dd);
+        mv[u] = ld_dev<float>(part, s0 + hd);
+        lv[u] = ld_dev<float>(part, s0 + hd + 1);
       }
+      float Mb = M;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < nch) o = fmaf(ml[2 * ((c0 + u) * hc + h)], v[u], o);
+      for (int u = 0; u < CB; ++u)
+        if (c0 + u < nch) Mb = fmaxf(Mb, mv[u]);
+      const float sc = (M == Mb) ? 1.f : __expf(M - Mb);  // M = -inf -> 0
+      lam *= sc;
+      O *= sc;
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (c0 + u < nch) {
+          const float w = mv[u] == -INFINITY ? 0.f : __expf(mv[u] - Mb);
+          lam = fmaf(w, lv[u], lam);
+          O = fmaf(w, ov[u], O);
+        }
+      }
+      M = Mb;
     }
-    st_dev<float>(att, (size_t)b * Hq * hd + (size_t)(h0 + h) * hd + dd, o / Mh[hc + h]);
+    st_dev<float>(att, (size_t)b * Hq * hd + (size_t)(h0 + h) * hd + dd, O / lam);
   }
 }
 

@@ -180,14 +180,10 @@ __device__ __forceinline__ void gemv_flush(const GemvGeom& g, const float park[B
   }
 }
 
-// A row is SEG segments of KBT kblocks (compile time; KBT = 0: any K, one kblock at a
-// time); RPG rows are in flight per wave.  Ring slot (r, kb) cycles through kblock
-// s * KBT + kb of row r for s = 0 .. SEG-1, then moves to the row RPG ahead.
-template <int BM, bool BF16, int KBT, int SEG, int RPG>
-__device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+// Geometry of this wave's share of GEMV tile d.
+template <bool BF16>
+__device__ __forceinline__ GemvGeom gemv_geom(const LaunchArgs& a, const mk_task_t& d) {
   constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int KBS = KBT > 0 ? KBT : 1;
-  const int lane = lane_id();
   GemvGeom g;
   g.wave = wave_id();
   g.W = resolve(a, d.in_buf[1]);
@@ -200,6 +196,68 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
   const int cnt = (int)d.reserved[1];
   g.nout = cnt > g.wave ? (cnt - g.wave + kWaves - 1) / kWaves : 0;
   g.NQ = g.nout << g.silu;
+  return g;
+}
+
+// Static-input prefetch into LDS of a tile whose rows have KBR kblocks (compile-time
+// streaming path): when the whole batch is staged in one pass and the wave has at most
+// 64 rows, the LDS after the staged input (xfl floats) holds the wave's first PF
+// whole rows at pfw.  One definition serves the tile itself and a prefetch issued
+// while the workgroup still runs its previous task.
+struct GemvPf {
+  int PF;
+  int xfl;
+  char* pfw;
+};
+
+template <int KBR>
+__device__ __forceinline__ GemvPf gemv_pf_plan(const GemvGeom& g, int B, int bp, Smem& sm) {
+  GemvPf p{0, 0, nullptr};
+  if (B <= bp && g.NQ <= 64) {
+    p.xfl = (B * g.K + 3) & ~3;
+    const int per_wave = ((kSmemBytes - 4 * p.xfl) / kWaves) & ~1023;
+    const int pf = per_wave / (KBR * 1024);
+    p.PF = pf < g.NQ ? pf : g.NQ;
+    p.pfw = (char*)(sm.xs + p.xfl) + g.wave * per_wave;
+  }
+  return p;
+}
+
+template <int KBR>
+__device__ __forceinline__ void gemv_issue_pf(const GemvGeom& g, const GemvPf& p, int lane) {
+  for (int q = 0; q < p.PF; ++q)
+#pragma unroll
+    for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(g, q, kb, lane, p.pfw + (q * KBR + kb) * 1024);
+}
+
+// Batch rows staged per pass of a tile with inner dimension K.
+template <int BM>
+__device__ __forceinline__ int gemv_batch_pass(int K) {
+  const int bp = (kSmemBytes / 4) / K;
+  return bp < BM ? bp : BM;
+}
+
+// Issue the LDS prefetch of GEMV tile d (rows of KBR kblocks) ahead of time, while the
+// workgroup still runs a task that uses at most lds_used bytes at the start of the
+// LDS.  Returns whether it was issued; the tile then skips its own prefetch.
+template <int BM, bool BF16, int KBR>
+__device__ __forceinline__ bool gemv_prefetch_ahead(const LaunchArgs& a, const mk_task_t& d, int lds_used,
+                                                    Smem& sm) {
+  const GemvGeom g = gemv_geom<BF16>(a, d);
+  const GemvPf p = gemv_pf_plan<KBR>(g, d.m, gemv_batch_pass<BM>(d.k), sm);
+  if (p.PF <= 0 || 4 * p.xfl < lds_used) return false;
+  gemv_issue_pf<KBR>(g, p, lane_id());
+  return true;
+}
+
+// A row is SEG segments of KBT kblocks (compile time; KBT = 0: any K, one kblock at a
+// time); RPG rows are in flight per wave.  Ring slot (r, kb) cycles through kblock
+// s * KBT + kb of row r for s = 0 .. SEG-1, then moves to the row RPG ahead.
+template <int BM, bool BF16, int KBT, int SEG, int RPG>
+__device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
+  constexpr int KBS = KBT > 0 ? KBT : 1;
+  const int lane = lane_id();
+  const GemvGeom g = gemv_geom<BF16>(a, d);
   const int KB = KBT > 0 ? KBT : (g.KC + 63) >> 6;
   const int N = d.n, B = d.m;
   const float* x = (const float*)resolve(a, d.in_buf[0]);
@@ -207,27 +265,20 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
   float* y = (float*)resolve(a, d.out_buf);
   const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
-  int bp = (kSmemBytes / 4) / g.K;
-  bp = bp < BM ? bp : BM;
+  const int bp = gemv_batch_pass<BM>(g.K);
 
   for (int b0 = 0; b0 < B; b0 += bp) {
     const int nb = (B - b0) < bp ? (B - b0) : bp;
-    // Static-input prefetch into LDS: the LDS left after the staged input holds the
-    // wave's first PF whole rows, loaded before the dependency wait (single-pass tiles
-    // of at most 64 rows per wave).  Those rows are consumed last, after the register
-    // ring has streamed the rest.
-    // The register ring's first rows are issued before the LDS rows: loads complete in
-    // issue order, so the ring never waits behind the prefetch.
+    // Static-input prefetch into LDS (gemv_pf_plan), loaded before the dependency
+    // wait, or already in flight when the previous task issued it (pre).  Those rows
+    // are consumed last, after the register ring has streamed the rest.  The register
+    // ring's first rows are issued before the LDS rows: loads complete in issue order,
+    // so the ring never waits behind the prefetch.
     constexpr int KBR = KBS * SEG;  // kblocks per row (compile-time path)
-    int PF = 0;
-    char* pfw = nullptr;
-    if (KBT > 0 && b0 == 0 && nb == B && g.NQ <= 64) {
-      const int xfl = (B * g.K + 3) & ~3;
-      const int per_wave = ((kSmemBytes - 4 * xfl) / kWaves) & ~1023;
-      PF = per_wave / (KBR * 1024);
-      PF = PF < g.NQ ? PF : g.NQ;
-      pfw = (char*)(sm.xs + xfl) + g.wave * per_wave;
-    }
+    GemvPf pf{0, 0, nullptr};
+    if (KBT > 0 && b0 == 0) pf = gemv_pf_plan<KBR>(g, B, bp, sm);
+    const int PF = pf.PF;
+    char* const pfw = pf.pfw;
     u32x4 buf[RPG][KBS];
     if (KBT > 0 && g.NQ > PF) {
 #pragma unroll
@@ -235,11 +286,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, PF + r, kb, lane);
     }
-    if (KBT > 0) {
-      for (int q = 0; q < PF; ++q)
-#pragma unroll
-        for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(g, q, kb, lane, pfw + (q * KBR + kb) * 1024);
-    }
+    if (KBT > 0 && !pre) gemv_issue_pf<KBR>(g, pf, lane);
     if (b0 == 0 && !dep_wait(a, t, d.remaining_deps, sm)) return;
     float rs[BM];
     gemv_stage<BM>(x, aux, d.config_id != MK_GEMV_F32, norm, g.K, b0, nb, a.rms_eps, sm, rs);
@@ -294,7 +341,9 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
       }
       if (KBT > 0) {
         // The LDS-resident rows (PF > 0 only when the wave has at most 64 rows, so the
-        // final flush covers them).
+        // final flush covers them).  Rows prefetched by the previous task were issued
+        // in another branch of the interpreter loop: wait for them explicitly.
+        if (pre) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         for (int q = 0; q < PF; ++q) {
           float acc[BM];
 #pragma unroll

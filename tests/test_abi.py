@@ -63,6 +63,7 @@ def test_abi_mismatch_fails_loudly():
     (dict(head_dim=63), "head_dim"),
     (dict(kv_chunk=100_000), "kv_chunk"),
     (dict(vocab=20_000_000), "4 GiB"),
+    (dict(kv_capacity=1 << 24), "KV head"),
 ])
 def test_invalid_configs_rejected(over, msg):
     cfg, keep = _cfg(workloads.tiny(), **over)
