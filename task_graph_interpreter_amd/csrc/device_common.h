@@ -56,9 +56,8 @@ struct Smem {
 
 struct LaunchArgs {
   const mk_task_t* tasks;
-  // Dependents array as uploaded, with bit 31 set on edges whose child is a NOP join
-  // (the CSR indices are unchanged; the flag saves a descriptor load per edge).
-  const uint32_t* edges;
+  const uint32_t* edges;      // dependents array (CSR, as lowered)
+  const uint32_t* join;       // per task: its NOP join parent, or 0xFFFFFFFF
   const uint32_t* order;      // static schedule: task lists grouped by workgroup
   const uint32_t* order_off;  // [grid + 1]; null = dynamic tickets
   const uint64_t* table;
@@ -268,40 +267,50 @@ __device__ __forceinline__ uint32_t read_status(const LaunchArgs& a) {
   return __hip_atomic_load((MK_GLOBAL uint32_t*)&a.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until task t's counter shows all of this step's parents have arrived
-// (arrivals[t] - epoch * indeg >= 0 in wrapping 32-bit arithmetic).  The producers'
-// data was written at device scope and acknowledged before their increments, and
-// every wave reads it with device-scope loads issued after the closing barrier, so
-// no cache invalidate is needed.  Bounded: on timeout (or if another workgroup raised
-// an error) the step is abandoned.  Returns false if the step was abandoned.  Called
-// by all threads.
+// Poll one readiness counter until it reaches target (wrapping 32-bit comparison),
+// bounded by the wait limit and abandoned if another workgroup raised an error.
+// Thread 0 only; returns 0 if the step was abandoned.
+__device__ __forceinline__ uint32_t poll_counter(const LaunchArgs& a, uint32_t t, const uint32_t* counter,
+                                                 uint32_t target) {
+  MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)counter;
+  uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((int32_t)(v - target) >= 0) return 1;
+  const uint64_t t0 = clock100();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - target) >= 0) return 1;
+    if (clock100() - t0 > a.wait_limit) {
+      raise_status(a, MK_STATUS_TIMEOUT | t);
+      return 0;
+    }
+    if (read_status(a) != 0) return 0;
+  }
+}
+
+// Wait until all of this step's parents of task t have arrived.  A task whose parents
+// include a NOP join (at most one: one join per op) waits for the join's own counter
+// to reach epoch * indeg(join) -- the join's parents count on it directly, nobody
+// fires it -- and for its own counter to reach epoch * (indeg - 1); any other task
+// waits for epoch * indeg on its own counter.  The producers' data was written at
+// device scope and acknowledged before their increments, and every wave reads it with
+// device-scope loads issued after the closing barrier, so no cache invalidate is
+// needed.  Bounded: on timeout (or if another workgroup raised an error) the step is
+// abandoned.  Returns false if the step was abandoned.  Called by all threads.
 __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_t indeg, Smem& sm) {
   if (indeg == 0) {
     if (threadIdx.x == 0) sm.t_ready = clock100();
     return true;
   }
   if (threadIdx.x == 0) {
-    MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + (size_t)t * kArrivalStride;
-    const uint32_t target = a.epoch * (uint32_t)indeg;
-    uint32_t ok = 1;
-    uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int32_t)(v - target) < 0) {
-      const uint64_t t0 = clock100();
-      for (;;) {
-        __builtin_amdgcn_s_sleep(1);
-        v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((int32_t)(v - target) >= 0) break;
-        if (clock100() - t0 > a.wait_limit) {
-          raise_status(a, MK_STATUS_TIMEOUT | t);
-          ok = 0;
-          break;
-        }
-        if (read_status(a) != 0) {
-          ok = 0;
-          break;
-        }
-      }
+    const uint32_t j = ldg<uint32_t>(a.join, t);
+    uint32_t ok = 1, own = (uint32_t)indeg;
+    if (j != 0xFFFFFFFFu) {
+      const uint32_t jdeg = ldg<uint32_t>(a.tasks, (size_t)j * 16 + 2);  // remaining_deps
+      ok = poll_counter(a, t, a.arrivals + (size_t)j * kArrivalStride, a.epoch * jdeg);
+      own -= 1;
     }
+    if (ok && own > 0) ok = poll_counter(a, t, a.arrivals + (size_t)t * kArrivalStride, a.epoch * own);
     sm.flag = ok;
     sm.t_ready = clock100();
   }
@@ -309,44 +318,14 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
   return sm.flag != 0;
 }
 
-// Count one arrival on each of the n dependents listed at edges[off].  A NOP join is
-// never run as a task: the parent whose increment completes its count (the returned
-// old value is the last one short of epoch * indeg) fires it on the spot, counting
-// one arrival on each of the NOP's own dependents.  NOP joins never feed NOP joins
-// (checked when lowering), so this recursion is one level deep.  Wave 0 only; the
-// caller has waited for its own data stores to be acknowledged.
+// Count one arrival on each of the n dependents listed at edges[off] (a NOP join
+// counts like any task; its children poll its counter).  Wave 0 only; the caller has
+// waited for its own data stores to be acknowledged.
 __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t off, uint32_t n) {
-  const int lane = lane_id();
-  for (uint32_t i0 = 0; i0 < n; i0 += 64) {
-    const uint32_t i = i0 + lane;
-    uint32_t fire = 0xFFFFFFFFu;
-    if (i < n) {
-      const uint32_t e = ldg<uint32_t>(a.edges, off + i);
-      const uint32_t c = e & 0x7FFFFFFFu;
-      MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)a.arrivals + (size_t)c * kArrivalStride;
-      if (e >> 31) {
-        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t indeg = ldg<uint32_t>(a.tasks, (size_t)c * 16 + 2);  // remaining_deps
-        if (old + 1u == a.epoch * indeg) fire = c;
-      } else {
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    uint64_t pending = __ballot(fire != 0xFFFFFFFFu);
-    while (pending) {
-      const int src = __builtin_ctzll(pending);
-      pending &= pending - 1;
-      const uint32_t c = __builtin_amdgcn_readlane(fire, src);
-      // Every other parent's data reached the device coherence point before its
-      // increment, and those increments precede this one on the NOP's counter.
-      const uint32_t nd = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 3));
-      const uint32_t no = __builtin_amdgcn_readfirstlane(ldg<uint32_t>(a.tasks, (size_t)c * 16 + 4));
-      for (uint32_t j = lane; j < nd; j += 64) {
-        const uint32_t cc = ldg<uint32_t>(a.edges, no + j) & 0x7FFFFFFFu;
-        __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + (size_t)cc * kArrivalStride, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+  for (uint32_t i = lane_id(); i < n; i += 64) {
+    const uint32_t c = ldg<uint32_t>(a.edges, off + i);
+    __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + (size_t)c * kArrivalStride, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -74,7 +74,7 @@ int lower(const mk_model_cfg* cfg, Lowered& out);
 // increasing task order (so the topological-order deadlock argument holds per list).
 // Built by simulating list scheduling in emission order with a byte-count cost model:
 // each task goes to the workgroup that can start it earliest.  NOP joins get no
-// workgroup: their last-arriving parent fires them.
+// workgroup: their parents count on the join's counter and its children poll it.
 struct Schedule {
   std::vector<uint32_t> order;    // task indices, grouped by workgroup
   std::vector<uint32_t> offsets;  // [workers + 1]

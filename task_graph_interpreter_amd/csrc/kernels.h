@@ -105,7 +105,7 @@ __device__ __forceinline__ bool run_task_spec(const LaunchArgs& a, const mk_task
     case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
     case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
-    default: break;  // NOP joins never run as tasks: their last parent fires them
+    default: break;  // NOP joins never run as tasks: their children poll their counter
   }
   return ahead;
 }
@@ -135,7 +135,7 @@ __device__ __forceinline__ mk_task_t read_desc(const Smem& sm, int slot) {
 
 // The next task of this workgroup: the next entry of its static list, or (dynamic
 // mode) the next ticket of the device-wide counter.  NOP joins are skipped: their
-// last-arriving parent fires them.  Thread 0 only.
+// children poll the join's counter.  Thread 0 only.
 __device__ __forceinline__ uint32_t next_task(const LaunchArgs& a, uint32_t& pos, uint32_t end) {
   if (a.order_off) return pos < end ? ldg<uint32_t>(a.order, pos++) : 0xFFFFFFFFu;
   for (;;) {

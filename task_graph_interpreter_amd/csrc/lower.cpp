@@ -429,9 +429,8 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
   }
   gemv(x, H, bi.w_lm(), V, MK_FLAG_RMS_NORM_INPUT, bi.final_norm(), bi.logits());
   bld.finish();
-  // A NOP join is fired inline by the parent that completes its count, which then
-  // counts arrivals on the NOP's own dependents without further checks: a NOP must
-  // never feed another NOP.
+  // A NOP join never runs: its children poll its counter in place of its own
+  // arrival, which only works one level deep, so a NOP must never feed another NOP.
   for (const mk_task_t& d : L.tasks)
     if (d.op_id == MK_OP_NOP)
       for (int32_t i = 0; i < d.num_dependents; ++i)

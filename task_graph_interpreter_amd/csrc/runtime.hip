@@ -72,7 +72,7 @@ struct mk_graph {
   char* d_blob = nullptr;
   mk_task_t* d_tasks = nullptr;
   uint32_t* d_edges = nullptr;       // as lowered
-  uint32_t* d_edges_dev = nullptr;   // bit 31 set where the child is a NOP join
+  uint32_t* d_join = nullptr;        // per task: its NOP join parent, or 0xFFFFFFFF
   uint32_t* d_order = nullptr;       // static schedule lists
   uint32_t* d_order_off = nullptr;   // [grid + 1]
   mk::Schedule sched;
@@ -116,7 +116,8 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   mk::LaunchArgs a;
   std::memset(&a, 0, sizeof(a));
   a.tasks = g->d_tasks;
-  a.edges = g->d_edges_dev;
+  a.edges = g->d_edges;
+  a.join = g->d_join;
   if (g->sched_mode == MK_SCHED_STATIC) {
     a.order = g->d_order;
     a.order_off = g->d_order_off;
@@ -255,25 +256,31 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   }
   const mk::Schedule& S = g->sched;
 
-  // One blob: 64-byte header, task array, edge array as lowered, the edge array the
-  // kernels read (NOP children flagged), the static lists and their offsets.
+  // One blob: 64-byte header, task array, edge array as lowered, each task's NOP join
+  // parent (a task has at most one: the lowering emits one join per op), the static
+  // lists and their offsets.
   const size_t nt = L.tasks.size(), ne = L.edges.size(), no = S.order.size();
-  std::vector<uint32_t> flagged(L.edges);
-  for (uint32_t& c : flagged)
-    if (L.tasks[c].op_id == MK_OP_NOP) c |= 0x80000000u;
+  std::vector<uint32_t> join(nt, 0xFFFFFFFFu);
+  for (size_t n = 0; n < nt; ++n) {
+    const mk_task_t& d = L.tasks[n];
+    if (d.op_id != MK_OP_NOP) continue;
+    for (int32_t i = 0; i < d.num_dependents; ++i) {
+      const uint32_t c = L.edges[(size_t)d.dependents_offset + i];
+      if (join[c] != 0xFFFFFFFFu) return fail(mk::set_error(MK_ERR_INVALID, "a task with two join parents"));
+      join[c] = (uint32_t)n;
+    }
+  }
   const size_t off_tasks = sizeof(mk::BlobHeader);
   const size_t off_edges = off_tasks + nt * sizeof(mk_task_t);
-  const size_t off_flagged = off_edges + ne * 4;
-  const size_t off_order = off_flagged + ne * 4;
+  const size_t off_join = off_edges + ne * 4;
+  const size_t off_order = off_join + nt * 4;
   const size_t off_order_off = off_order + no * 4;
   const size_t blob_bytes = off_order_off + S.offsets.size() * 4;
   std::vector<char> blob(blob_bytes);
   std::memcpy(blob.data(), &L.header, sizeof(mk::BlobHeader));
   std::memcpy(blob.data() + off_tasks, L.tasks.data(), nt * sizeof(mk_task_t));
-  if (ne) {
-    std::memcpy(blob.data() + off_edges, L.edges.data(), ne * 4);
-    std::memcpy(blob.data() + off_flagged, flagged.data(), ne * 4);
-  }
+  if (ne) std::memcpy(blob.data() + off_edges, L.edges.data(), ne * 4);
+  if (nt) std::memcpy(blob.data() + off_join, join.data(), nt * 4);
   if (no) std::memcpy(blob.data() + off_order, S.order.data(), no * 4);
   std::memcpy(blob.data() + off_order_off, S.offsets.data(), S.offsets.size() * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
@@ -283,7 +290,7 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
   g->d_tasks = (mk_task_t*)(g->d_blob + off_tasks);
   g->d_edges = (uint32_t*)(g->d_blob + off_edges);
-  g->d_edges_dev = (uint32_t*)(g->d_blob + off_flagged);
+  g->d_join = (uint32_t*)(g->d_blob + off_join);
   g->d_order = (uint32_t*)(g->d_blob + off_order);
   g->d_order_off = (uint32_t*)(g->d_blob + off_order_off);
   if ((e = hipMemcpyAsync(g->d_blob, blob.data(), blob_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)

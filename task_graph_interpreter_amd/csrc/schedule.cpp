@@ -59,7 +59,7 @@ void build_schedule(const Lowered& L, uint32_t workers, Schedule& S) {
     const mk_task_t& d = L.tasks[t];
     double fin;
     if (d.op_id == MK_OP_NOP) {
-      fin = ready[t];  // fired inline by its last parent
+      fin = ready[t];  // complete when its last parent counts on it
     } else {
       const Slot s = freeq.top();
       freeq.pop();
