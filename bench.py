@@ -171,6 +171,7 @@ def main():
     ap.add_argument("--trace-out", default=None, help="write a per-task trace of one step (.npy)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
     ap.add_argument("--gemv-tiles", type=int, default=0, help="override the workload's GEMV tiles per matmul")
+    ap.add_argument("--gemv-config", type=int, default=-1, help="override the GEMV variant (1 vector, 2 MFMA)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (byte-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -206,6 +207,8 @@ def main():
         w = w.replace(kv_chunk=args.kv_chunk)
     if args.gemv_tiles:
         w = w.replace(gemv_tiles=args.gemv_tiles)
+    if args.gemv_config >= 0:
+        w = w.replace(gemv_config=args.gemv_config)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
     inp = DeviceInputs(w)
@@ -296,7 +299,7 @@ def main():
         np.save(args.trace_out, tr.cpu().numpy().reshape(-1, 8))
         np.save(args.trace_out.replace(".npy", "_tasks.npy"), tasks)
 
-    traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles) else None
+    traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles or args.gemv_config >= 0) else None
 
     cpu = None
     if not args.no_cpu_baseline:

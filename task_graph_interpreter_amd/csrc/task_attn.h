@@ -258,33 +258,27 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
     }
   };
   // Batches of R rounds, double-buffered: the next batch's loads are issued before
-  // the current batch is folded.  Within a batch every load is unconditional (rows
-  // past the chunk are out of range and read nothing), so the compiler keeps 2R rounds
-  // in flight with counted waits.  The last batch issues no look-ahead: a load still
-  // in flight would hold up the workgroup barrier below by a memory round trip.
+  // the current batch is folded.  All loads are unconditional (rows past the chunk,
+  // including the last batch's look-ahead, are out of range and read nothing), so the
+  // compiler keeps 2R rounds in flight with counted waits.
   const int nbatch = (rounds + R - 1) / R;
   for (int bt = 0; bt < nbatch; ++bt) {
-    const bool more = bt + 1 < nbatch;
     u32x4 kn[R], vn[R];
-    if (more) {
-      const int jn = jbase + (bt + 1) * R * kpr;
+    const int jn = jbase + (bt + 1) * R * kpr;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        kn[r] = ldk(jn + r * kpr);
-        vn[r] = ldv(jn + r * kpr);
-      }
+    for (int r = 0; r < R; ++r) {
+      kn[r] = ldk(jn + r * kpr);
+      vn[r] = ldv(jn + r * kpr);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int j = jbase + (bt * R + r) * kpr;
       fold(kr[r], vr[r], j < n && j != jnew);
     }
-    if (more) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        kr[r] = kn[r];
-        vr[r] = vn[r];
-      }
+    for (int r = 0; r < R; ++r) {
+      kr[r] = kn[r];
+      vr[r] = vn[r];
     }
   }
   if (has_new && wave == 0) fold(knew, vnew, kl == 0);
