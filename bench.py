@@ -159,6 +159,44 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
             "launches": [len(fv["interpreter"]), len(wv["interpreter"])], "command": command}
 
 
+def greedy_run(w, inp, n_tokens, stream):
+    """Greedy decode of n_tokens tokens from the timed step's position onward, with a
+    graph lowered for n_tokens more cache slots on the same weights.  The loop never
+    touches the host: argmax (lowest index on ties) and the position update run on the
+    device between steps.  Returns time between tokens."""
+    import torch
+
+    import task_graph_interpreter_amd as mk
+    from synth.device import DeviceInputs
+
+    w2 = w.replace(kv_len=tuple(int(l) + n_tokens for l in w.kv_len), kv_capacity=w.kv_capacity + n_tokens)
+    inp2 = DeviceInputs(w2, weights=inp.weights)
+    cfg2, keep2 = mk.make_cfg(**w2.mk_fields())
+    plan2 = mk.mk_plan(cfg2)
+    scratch2 = torch.zeros(plan2["scratch_bytes"], dtype=torch.uint8, device="cuda")
+    g2 = mk.mk_build_graph(cfg2, inp2.weight_ptrs(), scratch2.data_ptr(), stream)
+    inp2.set_step(w.tokens(), w.positions())
+    ptrs2 = inp2.step_ptrs()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(n_tokens):
+        g2.mk_decode_step(stream, *ptrs2)
+        inp2.tokens.copy_(torch.argmax(inp2.logits, dim=-1).to(torch.int32))
+        inp2.positions.add_(1)
+    ev1.record()
+    torch.cuda.synchronize()
+    assert g2.mk_status() == 0
+    total = ev0.elapsed_time(ev1)
+    g2.close()
+    del keep2
+    log(f"greedy: {n_tokens} tokens, {total / n_tokens:.4f} ms between tokens")
+    return {"tokens": n_tokens, "ms_per_token": total / n_tokens, "tokens_per_s": w.batch * n_tokens / (total / 1e3),
+            "first_position": int(w.positions()[0]), "kv_slots": w2.kv_capacity,
+            "note": "graph lowered for kv_len + tokens (empty chunks until reached); argmax and position "
+                    "update on the device between steps"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +210,9 @@ def main():
     ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
     ap.add_argument("--gemv-tiles", type=int, default=0, help="override the workload's GEMV tiles per matmul")
     ap.add_argument("--gemv-config", type=int, default=-1, help="override the GEMV variant (1 vector, 2 MFMA)")
+    ap.add_argument("--greedy-tokens", type=int, default=-1,
+                    help="greedy decode of N tokens after the timed step (time between tokens); "
+                         "default 256 at batch 1, else 0")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (byte-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -296,8 +337,17 @@ def main():
         g.mk_decode_step(stream, *ptrs)
         torch.cuda.synchronize()
         g.mk_set_trace(None)
-        np.save(args.trace_out, tr.cpu().numpy().reshape(-1, 8))
+        trace = tr.cpu().numpy().reshape(-1, 8)
+        np.save(args.trace_out, trace)
         np.save(args.trace_out.replace(".npy", "_tasks.npy"), tasks)
+        from task_graph_interpreter_amd import trace as mktrace
+        summary = mktrace.summarize(trace, tasks)
+        with open(args.trace_out.replace(".npy", "_summary.json"), "w") as f:
+            json.dump(summary, f, indent=1)
+        log("trace summary:\n" + mktrace.format_summary(summary))
+
+    n_greedy = args.greedy_tokens if args.greedy_tokens >= 0 else (256 if w.batch == 1 else 0)
+    greedy = greedy_run(w, inp, n_greedy, stream) if n_greedy > 0 else None
 
     traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles or args.gemv_config >= 0) else None
 
@@ -332,6 +382,7 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "per_op_baseline": per_op,
         "other_schedule": alt,
+        "greedy": greedy,
         "cpu_baseline": cpu,
     }
     g.close()

@@ -16,12 +16,19 @@ class DeviceInputs:
     """Weights (canonical order), K/V caches [layers, batch, kv_heads, capacity, hd],
     tokens, positions and a logits buffer for workload ``w`` on ``device``."""
 
-    def __init__(self, w: "workloads.Workload", device: str = "cuda", fill: bool = True):
+    def __init__(self, w: "workloads.Workload", device: str = "cuda", fill: bool = True, weights=None):
+        """``weights``: reuse another instance's weight tensors (same model shape) and
+        allocate only caches, tokens, positions and logits."""
         self.w = w
         self.device = torch.device(device)
         stream = torch.cuda.current_stream(self.device).cuda_stream
         self.weights = []
-        for tid, name, shape, mean, std, dtype in w.weight_specs():
+        if weights is not None:
+            specs = w.weight_specs()
+            assert len(weights) == len(specs)
+            assert all(tuple(t.shape) == tuple(sp[2]) for t, sp in zip(weights, specs))
+            self.weights = list(weights)
+        for tid, name, shape, mean, std, dtype in (w.weight_specs() if weights is None else []):
             t = torch.empty(shape, dtype=_tdtype(dtype), device=self.device)
             if fill:
                 native.gpu_fill_flat(t.data_ptr(), t.numel(), 0, w.seed, tid, mean, std, dtype, stream)

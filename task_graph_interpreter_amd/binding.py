@@ -21,6 +21,19 @@ MK_OK, MK_ERR_ABI, MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP, MK_ERR_NOMEM, MK_ER
 MK_STATUS_TIMEOUT, MK_STATUS_BAD_POSITION, MK_STATUS_BAD_TOKEN = 0x10000000, 0x20000000, 0x30000000
 MK_STATUS_KIND_MASK = 0xF0000000
 MK_SCHED_STATIC, MK_SCHED_DYNAMIC = 0, 1
+# OpIds and flag bits of the descriptor (mk.h).
+(MK_OP_NOP, MK_OP_MEMCPY, MK_OP_GEMV, MK_OP_RMSNORM, MK_OP_ATTENTION, MK_OP_MLP, MK_OP_SAMPLE,
+ MK_OP_ATTENTION_APPEND, MK_OP_ATTENTION_PARTIAL, MK_OP_ATTENTION_COMBINE) = range(10)
+MK_FLAG_SILU_MUL, MK_FLAG_ADD_RESIDUAL, MK_FLAG_RMS_NORM_INPUT = 1, 2, 4
+# numpy mirror of mk_task_t (64 bytes), for reading the descriptor array on the host.
+MK_TASK_DTYPE = np.dtype({
+    "names": ["op_id", "config_id", "step", "flags", "remaining_deps", "num_dependents", "dependents_offset",
+              "in_buf", "out_buf", "m", "n", "k", "kv_len", "reserved"],
+    "formats": ["<u2", "<u2", "<u2", "<u2", "<i4", "<i4", "<u4", ("<u2", (3,)), "<u2", "<i4", "<i4", "<i4", "<i4",
+                ("<u4", (5,))],
+    "offsets": [0, 2, 4, 6, 8, 12, 16, 20, 26, 28, 32, 36, 40, 44],
+    "itemsize": 64,
+})
 MK_DTYPE = {"f32": 0, "bf16": 1}
 
 # Every symbol include/mk.h declares.
