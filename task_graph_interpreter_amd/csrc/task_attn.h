@@ -133,7 +133,7 @@ __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
 
 // One pass over the chunk for query heads [hg, hg + HM) of the group; the first pass
 // (hg == 0) prefetches before waiting on the producers.
-template <bool BF16, int HM, int LPK, int R>
+template <bool BF16, int HM, int LPK, int R, bool BATCHED>
 __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, int hg) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VEC = 16 / ES;
@@ -257,6 +257,58 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
       }
     }
   };
+  // The same for a batch of R rows at once (BATCHED): all R scores first, then one
+  // running-max update and one rescale of (l, o) per head, then the R weighted rows
+  // (one exp per row instead of two, one rescale per batch instead of one per row).
+  // Masked rows score -inf and weigh 0.  Used by the long-context kernel, whose chunks
+  // run many batches; the batch-1 kernel keeps the per-row step, whose smaller code
+  // leaves the register allocation of the GEMV loops in the same kernel alone.
+  auto fold_batch = [&](const u32x4 (&kb)[R], const u32x4 (&vb)[R], const bool (&okb)[R]) {
+    float sc[R][HM];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float kf[8];
+      unpack<BF16>(kb[r], kf);
+#pragma unroll
+      for (int h = 0; h < HM; ++h) {
+        if (h < hc) {
+          float sv = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sv = fmaf(kf[e], q[h][e], sv);
+          if constexpr (LPK > 0) sv = group_allsum<LPK>(sv);
+          else sv = group_allsum(sv, lpk);
+          sc[r][h] = okb[r] ? sv : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      if (h < hc) {
+        float mb = m[h];
+#pragma unroll
+        for (int r = 0; r < R; ++r) mb = fmaxf(mb, sc[r][h]);
+        const float al = (m[h] == mb) ? 1.f : __expf(m[h] - mb);  // m = -inf -> 0
+        l[h] *= al;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[h][e] *= al;
+        m[h] = mb;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float vf[8];
+      unpack<BF16>(vb[r], vf);
+#pragma unroll
+      for (int h = 0; h < HM; ++h) {
+        if (h < hc) {
+          const float p = (sc[r][h] == -INFINITY) ? 0.f : __expf(sc[r][h] - m[h]);
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+        }
+      }
+    }
+  };
   // Batches of R rounds, double-buffered: the next batch's loads are issued before
   // the current batch is folded.  All loads are unconditional (rows past the chunk,
   // including the last batch's look-ahead, are out of range and read nothing), so the
@@ -270,10 +322,20 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
       kn[r] = ldk(jn + r * kpr);
       vn[r] = ldv(jn + r * kpr);
     }
+    if constexpr (BATCHED) {
+      bool okb[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int j = jbase + (bt * R + r) * kpr;
-      fold(kr[r], vr[r], j < n && j != jnew);
+      for (int r = 0; r < R; ++r) {
+        const int j = jbase + (bt * R + r) * kpr;
+        okb[r] = j < n && j != jnew;
+      }
+      fold_batch(kr, vr, okb);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int j = jbase + (bt * R + r) * kpr;
+        fold(kr[r], vr[r], j < n && j != jnew);
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -342,28 +404,28 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   return true;
 }
 
-template <bool KVBF16, int LPK, int R>
+template <bool KVBF16, int LPK, int R, bool BATCHED>
 __device__ __forceinline__ void partial_heads(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   const int hc = (int)d.reserved[2];
   for (int hg = 0; hg < hc; hg += 4)
-    if (!partial_pass<KVBF16, 4, LPK, R>(a, d, t, sm, hg)) return;
+    if (!partial_pass<KVBF16, 4, LPK, R, BATCHED>(a, d, t, sm, hg)) return;
 }
 
 // Lanes per cache row (head_dim * element size / 16) as a compile-time constant for
 // the common shapes (head_dim 64 and 128), else a run-time value.
-template <bool KVBF16>
+template <bool KVBF16, bool BATCHED>
 __device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   // R rounds per batch: 2 for chunks of at most two rounds, else 4.
   const int lpk = d.n * (KVBF16 ? 2 : 4) / 16;
   const bool short_chunk = d.kv_len <= 2 * kWaves * (64 / lpk);
   if (lpk == 8) {
-    if (short_chunk) partial_heads<KVBF16, 8, 2>(a, d, t, sm);
-    else partial_heads<KVBF16, 8, 4>(a, d, t, sm);
+    if (short_chunk) partial_heads<KVBF16, 8, 2, BATCHED>(a, d, t, sm);
+    else partial_heads<KVBF16, 8, 4, BATCHED>(a, d, t, sm);
   } else if (lpk == 16) {
-    if (short_chunk) partial_heads<KVBF16, 16, 2>(a, d, t, sm);
-    else partial_heads<KVBF16, 16, 4>(a, d, t, sm);
+    if (short_chunk) partial_heads<KVBF16, 16, 2, BATCHED>(a, d, t, sm);
+    else partial_heads<KVBF16, 16, 4, BATCHED>(a, d, t, sm);
   } else {
-    partial_heads<KVBF16, 0, 4>(a, d, t, sm);
+    partial_heads<KVBF16, 0, 4, BATCHED>(a, d, t, sm);
   }
 }
 
