@@ -202,6 +202,8 @@ int validate_cfg(const mk_model_cfg* c) {
     if (K > 32768) return set_error(MK_ERR_INVALID, "GEMV inner dim above 32768 (LDS staging)");
     if (c->gemv_config == MK_GEMV_BF16_MFMA && K % 256)
       return set_error(MK_ERR_INVALID, "the MFMA GEMV needs every inner dim % 256 == 0 (chunks of 8 x 32)");
+    if (c->gemv_config == MK_GEMV_BF16_MFMA && (int64_t)c->batch * K * 4 >= (1ll << 32))
+      return set_error(MK_ERR_INVALID, "the MFMA GEMV reads its fp32 input rows with 32-bit offsets: batch x K x 4 >= 4 GiB");
   }
   // The GEMV addresses a weight matrix with 32-bit byte offsets.
   const int64_t H = c->hidden;

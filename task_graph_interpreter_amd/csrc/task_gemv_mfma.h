@@ -75,25 +75,30 @@ __device__ __forceinline__ u32x4 mfma_wload(const MfmaGeom& g, int gb, int c, in
 }
 
 // Input chunk c of batch rows [b0, b0 + 32), as loaded by one staging thread st
-// (0..255): float4 slots st + 256 i (row f / 64, k4 f % 64), i = 0..7, and the
-// gammas of its k4.  Loads are unconditional (rows past the batch re-read the last
-// row and are zeroed when staged; without the norm `gamma` points at any readable
-// buffer and is ignored), so the wait counts stay exact.
+// (0..255): float4 k4 = st % 64 of rows b0 + st / 64 + 4 i, i = 0..7, and the gammas
+// of its k4.  Loads are unconditional (rows past the batch re-read the last row and
+// are zeroed when staged; without the norm `gamma` points at any readable buffer and
+// is ignored), so the wait counts stay exact.  The input is read through a raw buffer
+// resource with 32-bit offsets computed here from an opaque row base, so the compiler
+// keeps no per-row pointers alive across the chunk loop.
 struct XChunk {
   f32x4 v[8];
   u32x2 gm;
 };
 
-__device__ __forceinline__ void mfma_xload(const float* x, const char* gamma, uint32_t K, int B, int b0, int c,
-                                           int st, XChunk& xr) {
+__device__ __forceinline__ void mfma_xload(__amdgpu_buffer_rsrc_t xr, const char* gamma, uint32_t K, int B, int b0,
+                                           int c, int st, XChunk& xr_out) {
+  int r0 = b0 + (st >> 6);
+  asm volatile("" : "+v"(r0));
+  const uint32_t col = (uint32_t)c * kMfmaKC * 4u + (uint32_t)(st & 63) * 16u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int f = st + 256 * i;
-    const int b = b0 + (f >> 6);
-    const int bc = b < B ? b : B - 1;
-    xr.v[i] = ldg<f32x4>(x, ((size_t)bc * K + (size_t)c * kMfmaKC) / 4 + (f & 63));
+    const int b = r0 + 4 * i;
+    const uint32_t row = (uint32_t)(b < B ? b : B - 1);
+    const uint32_t off = row * K * 4u + col;
+    xr_out.v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
   }
-  xr.gm = ldg<u32x2>(gamma, (size_t)c * (kMfmaKC / 4) + (st & 63));
+  xr_out.gm = ldg<u32x2>(gamma, (size_t)c * (kMfmaKC / 4) + (st & 63));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -107,12 +112,13 @@ __device__ __forceinline__ void mfma_xstage(const XChunk& xr, bool norm, bool co
                                             uint16_t* xb, float ss[8]) {
   const float g0 = norm ? bf16_lo(xr.gm.x) : 1.f, g1 = norm ? bf16_hi(xr.gm.x) : 1.f;
   const float g2 = norm ? bf16_lo(xr.gm.y) : 1.f, g3 = norm ? bf16_hi(xr.gm.y) : 1.f;
+  // Row st / 64 + 4 i, element 4 (st % 64): one base address, compile-time offsets.
+  uint16_t* base = xb + (st >> 6) * kMfmaXPitch + 4 * (st & 63);
+  const int br0 = b0 + (st >> 6);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int f = st + 256 * i;
-    const int br = f >> 6, k4 = f & 63;
     f32x4 v = xr.v[i];
-    if (b0 + br >= B) v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (br0 + 4 * i >= B) v = f32x4{0.f, 0.f, 0.f, 0.f};
     const float q = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
     ss[i] += count ? q : 0.f;
     const float u0 = v.x * g0, u1 = v.y * g1, u2 = v.z * g2, u3 = v.w * g3;
@@ -123,8 +129,8 @@ __device__ __forceinline__ void mfma_xstage(const XChunk& xr, bool norm, bool co
     hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
     lo.x = pack_bf16x2(u0 - __uint_as_float((uint32_t)h0 << 16), u1 - __uint_as_float((uint32_t)h1 << 16));
     lo.y = pack_bf16x2(u2 - __uint_as_float((uint32_t)h2 << 16), u3 - __uint_as_float((uint32_t)h3 << 16));
-    *(u32x2*)(xb + br * kMfmaXPitch + 4 * k4) = hi;
-    *(u32x2*)(xb + kMfmaXHalf + br * kMfmaXPitch + 4 * k4) = lo;
+    *(u32x2*)(base + 4 * i * kMfmaXPitch) = hi;
+    *(u32x2*)(base + kMfmaXHalf + 4 * i * kMfmaXPitch) = lo;
   }
 }
 
@@ -152,10 +158,21 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
   const char* gamma = norm ? aux : (const char*)x;
   uint16_t* xbuf = (uint16_t*)sm.xs;  // [kMfmaXBufs][hi, lo][32][kMfmaXPitch] bf16
+  // The input rows as a raw buffer (B x K fp32; B * K * 4 < 4 GiB, checked when lowering).
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((uint32_t)B * g.K * 4u), kRawBufferWord3);
   const int st = threadIdx.x - kMfmaComputeWaves * 64;  // staging thread index (staging waves)
 
-  u32x4 ring[D][G][2];
+  float* row_ss = sm.red + kRedFloats - 32;
+  float* part = sm.xs;  // [4 compute waves][G][2 halves][64 lanes][4]
+  // The two roles run in separate branches from the first load to the hand-off of
+  // their results, so the weight ring and accumulators (compute waves) and the staged
+  // input registers (staging waves) are never live at the same time and can share
+  // registers.  The branch is wave-uniform, and both sides execute the same sequence
+  // of barriers: the dependency wait's, one after the first input chunks are staged,
+  // one per chunk, and one before the partial sums are written.
   if (compute) {
+    u32x4 ring[D][G][2];
 #pragma unroll
     for (int dc = 0; dc < D; ++dc)
 #pragma unroll
@@ -163,31 +180,16 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           ring[dc][r][j] = mfma_wload(g, gb0 + r, dc < g.nc ? dc : g.nc - 1, 2 * w + j, lane);
-  }
-  if (first) {
-    if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
-    // The input is read with plain loads: drop stale L1/L2 lines first.
-    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __syncthreads();
-  }
-  float ss[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  XChunk xa, xb2;  // the next two input chunks to stage (staging waves)
-  if (!compute) {
-    mfma_xload(x, gamma, g.K, B, b0, 0, st, xa);
-    mfma_xload(x, gamma, g.K, B, b0, g.nc > 1 ? 1 : 0, st, xb2);
-    mfma_xstage(xa, norm, true, B, b0, st, xbuf, ss);
-    mfma_xload(x, gamma, g.K, B, b0, g.nc > 2 ? 2 : g.nc - 1, st, xa);
-    mfma_xstage(xb2, norm, g.nc > 1, B, b0, st, xbuf + kMfmaXBuf, ss);
-    mfma_xload(x, gamma, g.K, B, b0, g.nc > 3 ? 3 : g.nc - 1, st, xb2);
-  }
-  __syncthreads();
-  f32x4 acc[G][2];
+    if (first) {
+      if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
+      // The input is read with plain loads: drop stale L1/L2 lines first.
+      if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+    }
+    __syncthreads();  // the first input chunks are staged
+    f32x4 acc[G][2];
 #pragma unroll
-  for (int r = 0; r < G; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Separate loops for the two roles keep the weight ring and the staged input out of
-  // each other's registers; both execute one barrier per chunk.
-  if (compute) {
+    for (int r = 0; r < G; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < g.nc; c0 += U) {
 #pragma unroll
       for (int dc = 0; dc < U; ++dc) {
@@ -209,7 +211,26 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
         }
       }
     }
+    __syncthreads();  // every wave is done with the staged input; partial sums reuse it
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *(f32x4*)(part + (((w * G + r) * 2 + h) * 64 + lane) * 4) = acc[r][h];
   } else {
+    if (first) {
+      if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
+      __syncthreads();
+    }
+    float ss[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    XChunk xa, xb2;  // the next two input chunks to stage
+    mfma_xload(xrs, gamma, g.K, B, b0, 0, st, xa);
+    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 1 ? 1 : 0, st, xb2);
+    mfma_xstage(xa, norm, true, B, b0, st, xbuf, ss);
+    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 2 ? 2 : g.nc - 1, st, xa);
+    mfma_xstage(xb2, norm, g.nc > 1, B, b0, st, xbuf + kMfmaXBuf, ss);
+    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 3 ? 3 : g.nc - 1, st, xb2);
+    __syncthreads();  // the first input chunks are staged
     for (int c0 = 0; c0 < g.nc; c0 += U) {
 #pragma unroll
       for (int dc = 0; dc < U; ++dc) {
@@ -221,32 +242,22 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
           // an idle buffer and are not counted in ss.
           XChunk& xs = (dc & 1) ? xb2 : xa;  // c0 is even
           mfma_xstage(xs, norm, c + 2 < g.nc, B, b0, st, xbuf + ((c + 2) % kMfmaXBufs) * kMfmaXBuf, ss);
-          mfma_xload(x, gamma, g.K, B, b0, c + 4 < g.nc ? c + 4 : g.nc - 1, st, xs);
+          mfma_xload(xrs, gamma, g.K, B, b0, c + 4 < g.nc ? c + 4 : g.nc - 1, st, xs);
           __syncthreads();
         }
       }
     }
-  }
-
-  // Sum of squares of each staged batch row, kept in LDS for every group of this batch
-  // block (first group only: later groups restage the same rows).  Staging wave w'
-  // holds rows w' + 4 i, each lane one float4 of every chunk.
-  float* row_ss = sm.red + kRedFloats - 32;
-  if (need_ss && !compute) {
+    // Sum of squares of each staged batch row, kept in LDS for every group of this
+    // batch block (first group only: later groups restage the same rows).  Staging
+    // wave w' holds rows w' + 4 i, each lane one float4 of every chunk.
+    if (need_ss) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = wave_sum(ss[i]);
-      if (lane == 0) row_ss[(w - kMfmaComputeWaves) + 4 * i] = s;
+      for (int i = 0; i < 8; ++i) {
+        const float s = wave_sum(ss[i]);
+        if (lane == 0) row_ss[(w - kMfmaComputeWaves) + 4 * i] = s;
+      }
     }
-  }
-  __syncthreads();  // every wave is done with the staged input; partial sums reuse it
-  float* part = sm.xs;  // [4 compute waves][G][2 halves][64 lanes][4]
-  if (compute) {
-#pragma unroll
-    for (int r = 0; r < G; ++r)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *(f32x4*)(part + (((w * G + r) * 2 + h) * 64 + lane) * 4) = acc[r][h];
+    __syncthreads();  // every wave is done with the staged input; partial sums reuse it
   }
   __syncthreads();
 
