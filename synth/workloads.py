@@ -183,7 +183,7 @@ def llama8b() -> Workload:
 def llama8b_ragged(seed: int = 0) -> Workload:
     kv = _ragged_lengths(seed, 8, 512, 8192)
     return llama8b().replace(name="8b_b8_ragged", batch=8, kv_chunk=512, kv_len=kv,
-                             kv_capacity=max(kv), seed=seed)
+                             kv_capacity=max(kv), seed=seed, gemv_config=2)
 
 
 def llama8b_long() -> Workload:
