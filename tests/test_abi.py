@@ -64,6 +64,8 @@ def test_abi_mismatch_fails_loudly():
     (dict(kv_chunk=100_000), "kv_chunk"),
     (dict(vocab=20_000_000), "4 GiB"),
     (dict(kv_capacity=1 << 24), "KV head"),
+    (dict(batch=65536, kv_len=(128,) * 65536, weight_dtype="bf16", kv_dtype="bf16", gemv_config=2,
+          hidden=16384, n_q_heads=64, n_kv_heads=16), "batch x K x 4"),
 ])
 def test_invalid_configs_rejected(over, msg):
     cfg, keep = _cfg(workloads.tiny(), **over)
