@@ -192,9 +192,11 @@ int validate_cfg(const mk_model_cfg* c) {
     }
   }
   if (7ll + 15ll * c->n_layers > 0xFFFF) return set_error(MK_ERR_INVALID, "more than 65535 buffers");
-  // Limits of the device task bodies: GEMV rows are streamed in 16-byte pieces and the
-  // input row is staged in 128 KB of LDS; a KV row is read by a power-of-two group of
-  // lanes, 16 bytes each; a chunk's scores for the group's heads live in LDS.
+  // Limits of the device task bodies: GEMV rows are streamed in 16-byte pieces and an
+  // input row is staged in the 148 KB LDS area; a KV row is read by a power-of-two
+  // group of lanes, 16 bytes each.  The chunk length and the number of chunks have no
+  // device limit (a partial keeps its running sums in registers, a combine folds
+  // blocks of 16 chunks).
   const int64_t wes = c->weight_dtype == MK_DTYPE_F32 ? 4 : 2, kes = c->kv_dtype == MK_DTYPE_F32 ? 4 : 2;
   const int64_t Ks[3] = {c->hidden, (int64_t)c->n_q_heads * c->head_dim, c->intermediate};
   for (int64_t K : Ks) {
@@ -218,13 +220,6 @@ int validate_cfg(const mk_model_cfg* c) {
   const int64_t lpk = c->head_dim * kes / 16;
   if ((c->head_dim * kes) % 16 || lpk < 1 || lpk > 64 || (lpk & (lpk - 1)))
     return set_error(MK_ERR_INVALID, "head_dim * cache element size must be 16 * 2^j bytes, at most 1 KB");
-  const int64_t grp = c->n_q_heads / c->n_kv_heads;
-  if (grp * (c->head_dim + c->kv_chunk) + 8 * std::min<int64_t>(grp, 8) * c->head_dim > 32768)
-    return set_error(MK_ERR_INVALID, "kv_chunk too large for the attention partial's LDS");
-  // The combine stages every chunk's (m, l) for the group's heads in LDS.
-  const int64_t max_chunks = ((int64_t)c->kv_capacity + c->kv_chunk - 1) / c->kv_chunk;
-  if (max_chunks * grp * 2 > 32768 || 2 * grp > 1024)
-    return set_error(MK_ERR_INVALID, "too many KV chunks per head group for the combine's LDS (raise kv_chunk)");
   if (c->batch > (1 << 20) || c->kv_capacity > (1 << 30)) return set_error(MK_ERR_INVALID, "size too large");
   return MK_OK;
 }

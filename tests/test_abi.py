@@ -61,7 +61,7 @@ def test_abi_mismatch_fails_loudly():
     (dict(kv_len=(129,)), "kv_len"),
     (dict(gemv_config=1), "gemv_config"),
     (dict(head_dim=63), "head_dim"),
-    (dict(kv_chunk=100_000), "kv_chunk"),
+    (dict(kv_chunk=0), "kv_chunk"),
     (dict(vocab=20_000_000), "4 GiB"),
     (dict(kv_capacity=1 << 24), "KV head"),
     (dict(batch=65536, kv_len=(128,) * 65536, weight_dtype="bf16", kv_dtype="bf16", gemv_config=2,
