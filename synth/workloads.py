@@ -187,7 +187,7 @@ def llama8b_ragged(seed: int = 0) -> Workload:
 
 
 def llama8b_long() -> Workload:
-    return llama8b().replace(name="8b_b32_32k", batch=32, kv_chunk=4096, kv_len=(32768,) * 32,
+    return llama8b().replace(name="8b_b32_32k", batch=32, kv_chunk=8192, kv_len=(32768,) * 32,
                              kv_capacity=32768, gemv_config=2)
 
 
