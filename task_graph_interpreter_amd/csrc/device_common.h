@@ -61,6 +61,7 @@ struct LaunchArgs {
   const uint32_t* order;      // static schedule: task lists grouped by workgroup
   const uint32_t* order_off;  // [grid + 1]; null = dynamic tickets
   const uint64_t* table;
+  const float* rope;   // [kv_capacity][head_dim / 2] (cos, sin): RoPE coefficients per cache slot
   uint32_t* arrivals;  // one counter per kArrivalStride words
   Ctrl* ctrl;
   uint64_t* trace;

@@ -4,6 +4,7 @@
 // launch per op of the same task bodies (mk_decode_step_per_op, the baseline).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -75,6 +76,7 @@ struct mk_graph {
   uint32_t* d_join = nullptr;        // per task: its NOP join parent, or 0xFFFFFFFF
   uint32_t* d_order = nullptr;       // static schedule lists
   uint32_t* d_order_off = nullptr;   // [grid + 1]
+  float* d_rope = nullptr;           // [kv_capacity][head_dim / 2] (cos, sin) pairs
   mk::Schedule sched;
   int sched_mode = MK_SCHED_STATIC;
   uint64_t* d_table = nullptr;
@@ -123,6 +125,7 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
     a.order_off = g->d_order_off;
   }
   a.table = g->d_table;
+  a.rope = g->d_rope;
   a.arrivals = g->d_arrivals;
   a.ctrl = g->d_ctrl;
   a.trace = g->d_trace;
@@ -275,8 +278,25 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   const size_t off_join = off_edges + ne * 4;
   const size_t off_order = off_join + nt * 4;
   const size_t off_order_off = off_order + no * 4;
-  const size_t blob_bytes = off_order_off + S.offsets.size() * 4;
+  // RoPE coefficients of every cache slot: the angle pos * theta^(-2i/hd) and its
+  // cosine and sine in binary64, rounded to binary32.  They depend on the position
+  // only, so APPEND reads them (a static input) before its dependency wait instead of
+  // evaluating binary64 transcendentals on the critical path.
+  const size_t half = (size_t)L.cfg.head_dim / 2, cap = (size_t)L.cfg.kv_capacity;
+  const size_t off_rope = (off_order_off + S.offsets.size() * 4 + 15) & ~(size_t)15;
+  const size_t blob_bytes = off_rope + cap * half * 8;
   std::vector<char> blob(blob_bytes);
+  {
+    float* rope = (float*)(blob.data() + off_rope);
+    for (size_t i = 0; i < half; ++i) {
+      const double inv = std::pow((double)L.cfg.rope_theta, -2.0 * (double)i / (double)L.cfg.head_dim);
+      for (size_t pos = 0; pos < cap; ++pos) {
+        const double ang = (double)pos * inv;
+        rope[(pos * half + i) * 2] = (float)std::cos(ang);
+        rope[(pos * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    }
+  }
   std::memcpy(blob.data(), &L.header, sizeof(mk::BlobHeader));
   std::memcpy(blob.data() + off_tasks, L.tasks.data(), nt * sizeof(mk_task_t));
   if (ne) std::memcpy(blob.data() + off_edges, L.edges.data(), ne * 4);
@@ -293,6 +313,7 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   g->d_join = (uint32_t*)(g->d_blob + off_join);
   g->d_order = (uint32_t*)(g->d_blob + off_order);
   g->d_order_off = (uint32_t*)(g->d_blob + off_order_off);
+  g->d_rope = (float*)(g->d_blob + off_rope);
   if ((e = hipMemcpyAsync(g->d_blob, blob.data(), blob_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     return fail(hip_fail(e, "hipMemcpyAsync(blob)"));
   if ((e = hipMemcpyAsync(g->d_table, table.data(), table.size() * 8, hipMemcpyHostToDevice, s)) != hipSuccess)

@@ -11,19 +11,11 @@ namespace mk {
 // ---------------------------------------------------------------------------------
 // ATTENTION_APPEND (OpId 7 of the OpId table in "Mega kernel initial"): for sequence
 // b and KV head g, rotate the group's query heads and k_g (rotate-half RoPE, angle
-// pos * theta^(-2i/hd) with the angle and its sine/cosine evaluated in fp64), write
-// rotated q to q_rot and the rotated k and v into cache slot positions[b], rounded
-// to the cache dtype.
+// pos * theta^(-2i/hd)), write rotated q to q_rot and the rotated k and v into cache
+// slot positions[b], rounded to the cache dtype.  The cosine and sine of each angle
+// come from a per-slot table the host fills once per graph (binary64, rounded to
+// binary32); they depend on the position only, so they are loaded before the wait.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cs(int pos, int i, int hd, float theta, float& c, float& s) {
-  const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
-  const double ang = (double)pos * inv;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
-}
-
 __device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc = (int)d.reserved[2];
   const int g = d.k, hd = d.n, cap = d.kv_len;
@@ -34,14 +26,17 @@ __device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t
   char* vc = resolve(a, d.reserved[4]);
   // positions is a per-step input (no producer task): read it before waiting.
   const int pos = ldg<int32_t>((const void*)a.rt[TAG_POSITIONS], b);
-  // Rotation coefficients do not depend on producers either.
+  const bool bad = pos < 0 || pos >= cap;
+  // Rotation coefficients do not depend on producers either (a bad position reads
+  // slot 0 and is reported after the wait).
   const int half = hd / 2;
   const int nrot = (hc + 1) * half;
-  float cs_c = 0.f, cs_s = 0.f;
+  const size_t cs_row = (size_t)(bad ? 0 : pos) * half;
+  uint64_t cs0 = 0;  // (cos, sin) as two binary32 words
   const int e0 = threadIdx.x;
-  if (e0 < nrot) rope_cs(pos, e0 % half, hd, a.rope_theta, cs_c, cs_s);
+  if (e0 < nrot) cs0 = ldg<uint64_t>(a.rope, cs_row + e0 % half);
   if (!dep_wait(a, t, d.remaining_deps, sm)) return;
-  if (pos < 0 || pos >= cap) {
+  if (bad) {
     if (threadIdx.x == 0) raise_status(a, MK_STATUS_BAD_POSITION | t);
     return;
   }
@@ -52,8 +47,8 @@ __device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t
   for (int e = threadIdx.x; e < nrot + hd; e += kThreads) {
     if (e < nrot) {
       const int hh = e / half, i = e % half;
-      float c = cs_c, s = cs_s;
-      if (e != e0) rope_cs(pos, i, hd, a.rope_theta, c, s);
+      const uint64_t cs = e == e0 ? cs0 : ldg<uint64_t>(a.rope, cs_row + i);
+      const float c = __uint_as_float((uint32_t)cs), s = __uint_as_float((uint32_t)(cs >> 32));
       const size_t src = hh < hc ? row + (size_t)(h0 + hh) * hd : row + (size_t)(Hq + g) * hd;
       const float x0 = ld_dev<float>(qkv, src + i), x1 = ld_dev<float>(qkv, src + i + half);
       const float r0 = x0 * c - x1 * s;
@@ -91,34 +86,9 @@ __device__ __forceinline__ void task_append(const LaunchArgs& a, const mk_task_t
 // is loaded before the dependency wait; the new token's row (written by this step's
 // APPEND) is read after it and folded in last.  Each lane group keeps a running
 // (m, l, o) per head (the dot product is summed across the group with DPP moves);
-// groups are merged with the same log-sum-exp rule across the wavefront (xor
-// shuffles) and across wavefronts (LDS).
+// the states of all groups are merged with the same log-sum-exp rule in one pass
+// through LDS.
 // ---------------------------------------------------------------------------------
-
-__device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2, float l2, const float* o2,
-                                          int n) {
-  const float M = fmaxf(m, m2);
-  const float a1 = (m == -INFINITY) ? 0.f : __expf(m - M);
-  const float a2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - M);
-  l = l * a1 + l2 * a2;
-  for (int e = 0; e < n; ++e) o[e] = o[e] * a1 + o2[e] * a2;
-  m = M;
-}
-
-// Log-sum-exp merge of every lane's running state with that of lane ^ OFF.
-template <int OFF, int HM, int VEC>
-__device__ __forceinline__ void merge_groups(float (&m)[HM], float (&l)[HM], float (&o)[HM][8], int hc) {
-#pragma unroll
-  for (int h = 0; h < HM; ++h) {
-    if (h < hc) {
-      const float m2 = lane_xor<OFF>(m[h]), l2 = lane_xor<OFF>(l[h]);
-      float o2[8];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o2[e] = lane_xor<OFF>(o[h][e]);
-      lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
-    }
-  }
-}
 
 template <bool BF16>
 __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
@@ -345,61 +315,65 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   }
   if (has_new && wave == 0) fold(knew, vnew, kl == 0);
   trace_mark(a, sm, 0);
-  // Merge the lane groups of the wavefront (offsets lpk .. 32).
-  if constexpr (LPK > 0) {
-    if constexpr (LPK <= 1) merge_groups<1, HM, VEC>(m, l, o, hc);
-    if constexpr (LPK <= 2) merge_groups<2, HM, VEC>(m, l, o, hc);
-    if constexpr (LPK <= 4) merge_groups<4, HM, VEC>(m, l, o, hc);
-    if constexpr (LPK <= 8) merge_groups<8, HM, VEC>(m, l, o, hc);
-    if constexpr (LPK <= 16) merge_groups<16, HM, VEC>(m, l, o, hc);
-    if constexpr (LPK <= 32) merge_groups<32, HM, VEC>(m, l, o, hc);
-  } else {
-    for (int off = lpk; off < 64; off <<= 1) {
-#pragma unroll
-      for (int h = 0; h < HM; ++h) {
-        if (h < hc) {
-          const float m2 = __shfl_xor(m[h], off, 64), l2 = __shfl_xor(l[h], off, 64);
-          float o2[8];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(o[h][e], off, 64);
-          lse_merge(m[h], l[h], o[h], m2, l2, o2, VEC);
-        }
-      }
-    }
-  }
-  // Merge the wavefronts through LDS: o in [wave][head][hd] at the start of the
-  // staging area, (m, l) in [wave][head][2] in the reduction area.
+  // Merge the running states of every lane group of the workgroup in one LDS pass
+  // (log-sum-exp rule): each group writes its (m, l) and its slice of o, one wave per
+  // head turns the S = kWaves * kpw maxima into the head's M and per-state weights
+  // w_s = e^(m_s - M) (and L = sum_s w_s l_s) with wave reductions, and each thread
+  // then sums one output element over the S states.  Layout in the staging area:
+  // o as [S][HM][hd], then (m, l) as [S][HM][2], then w as [HM][S].
+  const int S = kWaves * kpw;
   float* po = sm.xs;
-  float* pml = sm.red;
-  if (!first) __syncthreads();  // the previous pass may still read po / pml
-  if (kl == 0) {
+  float* pml = po + (size_t)S * HM * hd;
+  float* pw = pml + (size_t)S * HM * 2;
+  if (!first) __syncthreads();  // the previous pass may still read po / pml / pw
+  {
+    const int st = wave * kpw + kl;
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
       if (h < hc) {
-        float* pw = po + ((size_t)wave * HM + h) * hd;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) pw[dl * VEC + e] = o[h][e];
+        float* dst = po + ((size_t)st * HM + h) * hd + dl * VEC;
+        *(f32x4*)dst = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+        if (VEC == 8) *(f32x4*)(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
         if (dl == 0) {
-          pml[(wave * HM + h) * 2] = m[h];
-          pml[(wave * HM + h) * 2 + 1] = l[h];
+          pml[(st * HM + h) * 2] = m[h];
+          pml[(st * HM + h) * 2 + 1] = l[h];
         }
       }
     }
   }
   __syncthreads();
-  trace_mark(a, sm, 1);
-  for (int e = threadIdx.x; e < hc * stride; e += kThreads) {
-    const int h = e / stride, dd = e % stride;
-    float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pml[(w * HM + h) * 2]);
-    float acc = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = pml[(w * HM + h) * 2];
-      const float al = (mw == -INFINITY) ? 0.f : __expf(mw - M);
-      if (dd < hd) acc = fmaf(po[((size_t)w * HM + h) * hd + dd], al, acc);
-      else if (dd == hd + 1) acc = fmaf(pml[(w * HM + h) * 2 + 1], al, acc);
+  if (wave < hc) {
+    const int h = wave;
+    float mx = -INFINITY;
+    for (int st = lane; st < S; st += 64) mx = fmaxf(mx, pml[(st * HM + h) * 2]);
+    mx = fmaxf(mx, lane_xor<32>(mx));
+    mx = fmaxf(mx, lane_xor<16>(mx));
+    mx = fmaxf(mx, lane_xor<8>(mx));
+    mx = fmaxf(mx, lane_xor<4>(mx));
+    mx = fmaxf(mx, lane_xor<2>(mx));
+    mx = fmaxf(mx, lane_xor<1>(mx));
+    float lsum = 0.f;
+    for (int st = lane; st < S; st += 64) {
+      const float ms = pml[(st * HM + h) * 2];
+      const float w = ms == -INFINITY ? 0.f : __expf(ms - mx);  // every state empty: M = -inf, all 0
+      pw[h * S + st] = w;
+      lsum = fmaf(w, pml[(st * HM + h) * 2 + 1], lsum);
     }
-    st_dev<float>(out, out0 + h * stride + dd, (dd == hd) ? M : acc);
+    lsum = wave_sum(lsum);
+    if (lane == 0) {
+      st_dev<float>(out, out0 + h * stride + hd, mx);
+      st_dev<float>(out, out0 + h * stride + hd + 1, lsum);
+    }
+  }
+  __syncthreads();
+  trace_mark(a, sm, 1);
+  for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
+    const int h = e / hd, dd = e % hd;
+    const float* wh = pw + h * S;
+    const float* oh = po + (size_t)h * hd + dd;
+    float acc = 0.f;
+    for (int st = 0; st < S; ++st) acc = fmaf(oh[(size_t)st * HM * hd], wh[st], acc);
+    st_dev<float>(out, out0 + h * stride + dd, acc);
   }
   return true;
 }
