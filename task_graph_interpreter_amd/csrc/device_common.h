@@ -289,30 +289,38 @@ __device__ __forceinline__ uint32_t poll_counter(const LaunchArgs& a, uint32_t t
   }
 }
 
-// Wait until all of this step's parents of task t have arrived.  A task whose parents
+// Poll until all of this step's parents of task t have arrived.  A task whose parents
 // include a NOP join (at most one: one join per op) waits for the join's own counter
 // to reach epoch * indeg(join) -- the join's parents count on it directly, nobody
 // fires it -- and for its own counter to reach epoch * (indeg - 1); any other task
-// waits for epoch * indeg on its own counter.  The producers' data was written at
-// device scope and acknowledged before their increments, and every wave reads it with
-// device-scope loads issued after the closing barrier, so no cache invalidate is
-// needed.  Bounded: on timeout (or if another workgroup raised an error) the step is
-// abandoned.  Returns false if the step was abandoned.  Called by all threads.
+// waits for epoch * indeg on its own counter.  One thread; returns 0 if the step was
+// abandoned (timeout, or another workgroup raised an error).
+__device__ __forceinline__ uint32_t poll_deps(const LaunchArgs& a, uint32_t t, int32_t indeg) {
+  if (indeg == 0) return 1;
+  const uint32_t j = ldg<uint32_t>(a.join, t);
+  uint32_t ok = 1, own = (uint32_t)indeg;
+  if (j != 0xFFFFFFFFu) {
+    const uint32_t jdeg = ldg<uint32_t>(a.tasks, (size_t)j * 16 + 2);  // remaining_deps
+    ok = poll_counter(a, t, a.arrivals + (size_t)j * kArrivalStride, a.epoch * jdeg);
+    own -= 1;
+  }
+  if (ok && own > 0) ok = poll_counter(a, t, a.arrivals + (size_t)t * kArrivalStride, a.epoch * own);
+  return ok;
+}
+
+// Wait until all of this step's parents of task t have arrived (thread 0 polls).  The
+// producers' data was written at device scope and acknowledged before their
+// increments, and every wave reads it with device-scope loads issued after the
+// closing barrier, so no cache invalidate is needed.  Bounded: on timeout (or if
+// another workgroup raised an error) the step is abandoned.  Returns false if the
+// step was abandoned.  Called by all threads.
 __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_t indeg, Smem& sm) {
   if (indeg == 0) {
     if (threadIdx.x == 0) sm.t_ready = clock100();
     return true;
   }
   if (threadIdx.x == 0) {
-    const uint32_t j = ldg<uint32_t>(a.join, t);
-    uint32_t ok = 1, own = (uint32_t)indeg;
-    if (j != 0xFFFFFFFFu) {
-      const uint32_t jdeg = ldg<uint32_t>(a.tasks, (size_t)j * 16 + 2);  // remaining_deps
-      ok = poll_counter(a, t, a.arrivals + (size_t)j * kArrivalStride, a.epoch * jdeg);
-      own -= 1;
-    }
-    if (ok && own > 0) ok = poll_counter(a, t, a.arrivals + (size_t)t * kArrivalStride, a.epoch * own);
-    sm.flag = ok;
+    sm.flag = poll_deps(a, t, indeg);
     sm.t_ready = clock100();
   }
   __syncthreads();

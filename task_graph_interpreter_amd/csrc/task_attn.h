@@ -371,8 +371,20 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
     const int h = e / hd, dd = e % hd;
     const float* wh = pw + h * S;
     const float* oh = po + (size_t)h * hd + dd;
+    // Blocks of 8 states: the LDS reads of a block are issued together.
     float acc = 0.f;
-    for (int st = 0; st < S; ++st) acc = fmaf(oh[(size_t)st * HM * hd], wh[st], acc);
+    int st = 0;
+    for (; st + 8 <= S; st += 8) {
+      float ov[8], wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ov[u] = oh[(size_t)(st + u) * HM * hd];
+        wv[u] = wh[st + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(ov[u], wv[u], acc);
+    }
+    for (; st < S; ++st) acc = fmaf(oh[(size_t)st * HM * hd], wh[st], acc);
     st_dev<float>(out, out0 + h * stride + dd, acc);
   }
   return true;

@@ -18,11 +18,16 @@
 //    the hardware answers with zeros and no memory access (its result is discarded);
 //  * the ring's first fill is issued before the dependency wait: weights are static,
 //    so the tile's first bytes arrive while its producers are still finishing;
-//  * the input rows are staged once per task in LDS (fp32, x * gamma);
+//  * one wave (the control wave) waits for the producers and stages the input rows
+//    in LDS (fp32, x * gamma) while the other waves' bulk prefetch is still landing:
+//    a wave's loads complete in issue order, so a poll or staging load queued behind
+//    the prefetch would only start once the prefetch had arrived;
 //  * a finished row is reduced across the wavefront with DPP (no LDS traffic) and
 //    parked in the register of lane (row % 64); parked results are stored 64 at a
 //    time, outside the streaming loop for every shape the workloads use.
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -32,6 +37,13 @@ namespace mk {
 // lowering, rows a multiple of 16 bytes) is below it; kPastEnd is not.
 constexpr uint32_t kWeightRange = 0xFFFFFFF0u;
 constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+// The wave that waits for a tile's producers and stages its input (it streams its own
+// rows too, but issues no LDS prefetch: see gemv_issue_pf).
+constexpr int kCtrlWave = kWaves - 1;
+// Cache-policy operand of a device-scope (sc1) load.
+constexpr int kCachePolicySC1 = 16;
+// s_waitcnt operand: vector memory counter 0, the others unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct GemvGeom {
   const char* W;
@@ -100,57 +112,83 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
   }
 }
 
-// Stage input rows b0 .. b0+nb-1 of x (x * gamma with RMS_NORM_INPUT) into LDS and
-// return r_b (1 without the norm) in rs[].
-template <int BM>
-__device__ __forceinline__ void gemv_stage(const float* x, const char* gamma, bool gamma_bf16, bool norm, int K,
-                                           int b0, int nb, float eps, Smem& sm, float rs[BM]) {
-  float ss[BM];
+// Wait for the tile's producers and stage its input rows 0 .. nb-1 (x * gamma with
+// RMS_NORM_INPUT) into LDS, both on the control wave alone, then meet the other waves
+// at one barrier; returns r_b (1 without the norm) in rs[], or false if the step was
+// abandoned.  The control wave has issued no LDS prefetch, so its poll and its staging
+// loads queue only behind its own weight ring, not behind the tile's bulk prefetch,
+// which keeps arriving meanwhile.  The input rows are copied into LDS by device-scope
+// (sc1) global-to-LDS loads, up to 63 KB per round trip; gamma is loaded alongside
+// into registers in blocks of GB chunks of 4 values per lane; the norm's sum of
+// squares is then taken from LDS and reduced within the wave.
+template <int BM, bool GBF16>
+__device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t, int32_t indeg, const float* x,
+                                                const char* gamma, bool norm, int K, int nb, float eps, Smem& sm,
+                                                float rs[BM]) {
+  if (wave_id() == kCtrlWave) {
+    const int lane = lane_id();
+    uint32_t ok = 1;
+    if (lane == 0) {
+      ok = poll_deps(a, t, indeg);
+      sm.flag = ok;
+      sm.t_ready = clock100();
+    }
+    ok = __builtin_amdgcn_readfirstlane(ok);
+    if (ok) {
+      const int K4 = K >> 2;
+      for (int b = 0; b < nb; ++b)
+        for (int c = 0; c < K4; c += 64)
+          if (c + lane < K4)
+            __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL f32x4*)x + (size_t)b * K4 + c + lane),
+                                             (__attribute__((address_space(3))) void*)(sm.xs + (size_t)b * K + 4 * c),
+                                             16, 0, kCachePolicySC1);
+      // gamma (weight dtype) in raw form: 8 bytes per 4 values in bf16, 16 in fp32.
+      typedef typename std::conditional<GBF16, u32x2, u32x4>::type graw_t;
+      constexpr int GB = 16;
+      for (int b = 0; b < nb; ++b) {
+        f32x4* xo = (f32x4*)(sm.xs + (size_t)b * K);
+        float ss = 0.f;
+        for (int c0 = 0; c0 < K4; c0 += 64 * GB) {
+          graw_t gv[GB];
+          if (norm) {
 #pragma unroll
-  for (int b = 0; b < BM; ++b) ss[b] = 0.f;
-  const int K4 = K >> 2;
-#pragma unroll
-  for (int b = 0; b < BM; ++b) {
-    if (b < nb) {
-      f32x4* xo = (f32x4*)(sm.xs + b * K);
-      for (int k4 = threadIdx.x; k4 < K4; k4 += kThreads) {
-        f32x4 v = ld_dev_f4(x, (size_t)(b0 + b) * K4 + k4);
-        if (norm) {
-          ss[b] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[b]))));
-          float g0, g1, g2, g3;
-          if (gamma_bf16) {
-            const u32x2 gv = ldg<u32x2>(gamma, k4);
-            g0 = bf16_lo(gv.x); g1 = bf16_hi(gv.x); g2 = bf16_lo(gv.y); g3 = bf16_hi(gv.y);
-          } else {
-            const f32x4 gv = ldg<f32x4>(gamma, k4);
-            g0 = gv.x; g1 = gv.y; g2 = gv.z; g3 = gv.w;
+            for (int u = 0; u < GB; ++u) {
+              const int k4 = c0 + u * 64 + lane;
+              gv[u] = ldg<graw_t>(gamma, k4 < K4 ? k4 : 0);
+            }
           }
-          v.x *= g0; v.y *= g1; v.z *= g2; v.w *= g3;
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row's LDS copy has landed
+          if (norm) {
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+              const int k4 = c0 + u * 64 + lane;
+              if (k4 < K4) {
+                f32x4 v = xo[k4];
+                ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+                f32x4 gf;
+                if constexpr (GBF16) gf = f32x4{bf16_lo(gv[u].x), bf16_hi(gv[u].x), bf16_lo(gv[u].y), bf16_hi(gv[u].y)};
+                else gf = f32x4{__uint_as_float(gv[u].x), __uint_as_float(gv[u].y), __uint_as_float(gv[u].z),
+                                __uint_as_float(gv[u].w)};
+                xo[k4] = v * gf;
+              }
+            }
+          }
         }
-        xo[k4] = v;
+        if (norm) ss = wave_sum(ss);
+        if (lane == 0) sm.red[b] = norm ? 1.0f / sqrtf(ss / (float)K + eps) : 1.f;
       }
     }
   }
-  if (norm) {
-    const int w = wave_id();
-#pragma unroll
-    for (int b = 0; b < BM; ++b) ss[b] = wave_sum(ss[b]);
-    if (lane_id() == 0) {
-#pragma unroll
-      for (int b = 0; b < BM; ++b) sm.red[w * BM + b] = ss[b];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      float s = 0.f;
-      for (int i = 0; i < kWaves; ++i) s += sm.red[i * BM + b];
-      rs[b] = 1.0f / sqrtf(s / (float)K + eps);
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < BM; ++b) rs[b] = 1.f;
-  }
   __syncthreads();
+  // Every wave now waits for its own ring and LDS prefetch.  Written as the builtin
+  // (not inline asm) so that the compiler's wait-count tracking sees it: otherwise
+  // the prefetch's pending LDS writes would make it put a full wait before every LDS
+  // read of the staged input inside the streaming loop, draining the ring each step.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (sm.flag == 0) return false;
+#pragma unroll
+  for (int b = 0; b < BM; ++b) rs[b] = b < nb ? sm.red[b] : 1.f;
+  return true;
 }
 
 // Store the parked results of logical rows [q_base, q_base + 64) of this wave (lane l
@@ -182,10 +220,10 @@ __device__ __forceinline__ void gemv_flush(const GemvGeom& g, const float park[B
 
 // Geometry of this wave's share of GEMV tile d.
 template <bool BF16>
-__device__ __forceinline__ GemvGeom gemv_geom(const LaunchArgs& a, const mk_task_t& d) {
+__device__ __forceinline__ GemvGeom gemv_geom(const LaunchArgs& a, const mk_task_t& d, int wave) {
   constexpr int VEC = BF16 ? 8 : 4;
   GemvGeom g;
-  g.wave = wave_id();
+  g.wave = wave;
   g.W = resolve(a, d.in_buf[1]);
   g.wr = __builtin_amdgcn_make_buffer_rsrc((void*)g.W, (short)0, (int)kWeightRange, kRawBufferWord3);
   g.K = d.k;
@@ -223,11 +261,21 @@ __device__ __forceinline__ GemvPf gemv_pf_plan(const GemvGeom& g, int B, int bp,
   return p;
 }
 
+// Issue the LDS prefetch of the tile's PF-row blocks.  The control wave (which waits
+// for the producers and stages the input) issues none, so that nothing queues ahead of
+// its poll and its staging loads: the other waves issue their own rows and, round
+// robin, the control wave's (gc, pc: its geometry and plan).  Every wave waits for
+// its loads and meets a barrier before any LDS-resident row is read.
 template <int KBR>
-__device__ __forceinline__ void gemv_issue_pf(const GemvGeom& g, const GemvPf& p, int lane) {
+__device__ __forceinline__ void gemv_issue_pf(const GemvGeom& g, const GemvPf& p, const GemvGeom& gc,
+                                              const GemvPf& pc, int lane) {
+  if (g.wave == kCtrlWave) return;
   for (int q = 0; q < p.PF; ++q)
 #pragma unroll
     for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(g, q, kb, lane, p.pfw + (q * KBR + kb) * 1024);
+  for (int q = g.wave; q < pc.PF; q += kCtrlWave)
+#pragma unroll
+    for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(gc, q, kb, lane, pc.pfw + (q * KBR + kb) * 1024);
 }
 
 // Batch rows staged per pass of a tile with inner dimension K.
@@ -243,10 +291,13 @@ __device__ __forceinline__ int gemv_batch_pass(int K) {
 template <int BM, bool BF16, int KBR>
 __device__ __forceinline__ bool gemv_prefetch_ahead(const LaunchArgs& a, const mk_task_t& d, int lds_used,
                                                     Smem& sm) {
-  const GemvGeom g = gemv_geom<BF16>(a, d);
-  const GemvPf p = gemv_pf_plan<KBR>(g, d.m, gemv_batch_pass<BM>(d.k), sm);
-  if (p.PF <= 0 || 4 * p.xfl < lds_used) return false;
-  gemv_issue_pf<KBR>(g, p, lane_id());
+  const int bp = gemv_batch_pass<BM>(d.k);
+  const GemvGeom g = gemv_geom<BF16>(a, d, wave_id());
+  const GemvPf p = gemv_pf_plan<KBR>(g, d.m, bp, sm);
+  if (4 * p.xfl < lds_used) return false;
+  const GemvGeom gc = gemv_geom<BF16>(a, d, kCtrlWave);
+  const GemvPf pc = gemv_pf_plan<KBR>(gc, d.m, bp, sm);
+  gemv_issue_pf<KBR>(g, p, gc, pc, lane_id());
   return true;
 }
 
@@ -257,7 +308,7 @@ template <int BM, bool BF16, int KBT, int SEG, int RPG>
 __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
   constexpr int KBS = KBT > 0 ? KBT : 1;
   const int lane = lane_id();
-  const GemvGeom g = gemv_geom<BF16>(a, d);
+  const GemvGeom g = gemv_geom<BF16>(a, d, wave_id());
   const int KB = KBT > 0 ? KBT : (g.KC + 63) >> 6;
   const int N = d.n, B = d.m;
   const float* x = (const float*)resolve(a, d.in_buf[0]);
@@ -275,8 +326,13 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     // ring's first rows are issued before the LDS rows: loads complete in issue order,
     // so the ring never waits behind the prefetch.
     constexpr int KBR = KBS * SEG;  // kblocks per row (compile-time path)
-    GemvPf pf{0, 0, nullptr};
-    if (KBT > 0 && b0 == 0) pf = gemv_pf_plan<KBR>(g, B, bp, sm);
+    GemvPf pf{0, 0, nullptr}, pfc{0, 0, nullptr};
+    GemvGeom gc = g;
+    if (KBT > 0 && b0 == 0) {
+      pf = gemv_pf_plan<KBR>(g, B, bp, sm);
+      gc = gemv_geom<BF16>(a, d, kCtrlWave);
+      pfc = gemv_pf_plan<KBR>(gc, B, bp, sm);
+    }
     const int PF = pf.PF;
     char* const pfw = pf.pfw;
     u32x4 buf[RPG][KBS];
@@ -286,15 +342,20 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
 #pragma unroll
         for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, PF + r, kb, lane);
     }
-    if (KBT > 0 && !pre) gemv_issue_pf<KBR>(g, pf, lane);
-    if (b0 == 0 && !dep_wait(a, t, d.remaining_deps, sm)) return;
+    if (KBT > 0 && b0 == 0 && !pre) gemv_issue_pf<KBR>(g, pf, gc, pfc, lane);
     float rs[BM];
-    gemv_stage<BM>(x, aux, d.config_id != MK_GEMV_F32, norm, g.K, b0, nb, a.rms_eps, sm, rs);
+    // One call site for every batch pass (later passes have no producers to wait
+    // for): staging code duplicated on two paths into the streaming loop made the
+    // compiler's wait counts there drain the whole ring at every row.
+    if (!gemv_wait_stage<BM, BF16>(a, t, b0 == 0 ? d.remaining_deps : 0, x + (size_t)b0 * g.K, aux, norm, g.K, nb,
+                                   a.rms_eps, sm, rs))
+      return;
     if (b0 == 0) trace_mark(a, sm, 0);
-    if (g.NQ > 0) {
-      float park[BM];
+    float park[BM];
 #pragma unroll
-      for (int b = 0; b < BM; ++b) park[b] = 0.f;
+    for (int b = 0; b < BM; ++b) park[b] = 0.f;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // nothing pending into LDS (ring already landed)
+    if (g.NQ > 0) {
       const int iters_ring = (g.NQ - PF + RPG - 1) / RPG;
       for (int it = 0; it < iters_ring; ++it) {
         const int q0 = PF + it * RPG;
@@ -339,11 +400,17 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
             gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
         }
       }
+    }
+    // The LDS-resident rows (PF > 0 only when the whole batch is staged in one pass
+    // and the wave has at most 64 rows, so the final flush covers them).  They were
+    // loaded by other waves (the control wave's) or by the previous task: every wave
+    // waits for its own loads, then all meet, before any of them is read.
+    if (KBT > 0 && b0 == 0 && B <= bp) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+    if (g.NQ > 0) {
       if (KBT > 0) {
-        // The LDS-resident rows (PF > 0 only when the wave has at most 64 rows, so the
-        // final flush covers them).  Rows prefetched by the previous task were issued
-        // in another branch of the interpreter loop: wait for them explicitly.
-        if (pre) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         for (int q = 0; q < PF; ++q) {
           float acc[BM];
 #pragma unroll
