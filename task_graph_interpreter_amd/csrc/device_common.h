@@ -270,22 +270,27 @@ __device__ __forceinline__ uint32_t read_status(const LaunchArgs& a) {
 
 // Poll one readiness counter until it reaches target (wrapping 32-bit comparison),
 // bounded by the wait limit and abandoned if another workgroup raised an error.
-// Thread 0 only; returns 0 if the step was abandoned.
+// Thread 0 only; returns 0 if the step was abandoned.  A device-scope load is a
+// round trip to memory, so the loop's period is what a waiting task adds to its
+// producers' release: every iteration reads the counter alone, and only every 16th
+// also reads the clock and the status word.
 __device__ __forceinline__ uint32_t poll_counter(const LaunchArgs& a, uint32_t t, const uint32_t* counter,
                                                  uint32_t target) {
   MK_GLOBAL uint32_t* cnt = (MK_GLOBAL uint32_t*)counter;
   uint32_t v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((int32_t)(v - target) >= 0) return 1;
   const uint64_t t0 = clock100();
-  for (;;) {
+  for (uint32_t it = 1;; ++it) {
     __builtin_amdgcn_s_sleep(1);
     v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int32_t)(v - target) >= 0) return 1;
-    if (clock100() - t0 > a.wait_limit) {
-      raise_status(a, MK_STATUS_TIMEOUT | t);
-      return 0;
+    if ((it & 15u) == 0u) {
+      if (clock100() - t0 > a.wait_limit) {
+        raise_status(a, MK_STATUS_TIMEOUT | t);
+        return 0;
+      }
+      if (read_status(a) != 0) return 0;
     }
-    if (read_status(a) != 0) return 0;
   }
 }
 

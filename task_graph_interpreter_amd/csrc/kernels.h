@@ -186,19 +186,22 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
     mk_task_t dn;
     if (tn < a.n_tasks) dn = read_desc(sm, s1);
     uint64_t t_claim = 0;
-    uint32_t nn = 0xFFFFFFFFu;
+    uint32_t nn = 0xFFFFFFFFu, status = 0;
     if (threadIdx.x == 0) {
       if (trace) {
         t_claim = clock100();
         sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
       }
       if (tn < a.n_tasks) nn = next_task(a, pos, end);
+      // Read while the task runs: a read issued after the task body would hold up the
+      // release, which waits for all of the workgroup's outstanding memory operations.
+      status = read_status(a);
     }
     pre = run_task_spec<S>(a, d, t, sm, pre, tn < a.n_tasks ? &dn : nullptr);
     uint64_t t_end = 0;
     if (threadIdx.x == 0) {
       if (trace) t_end = clock100();
-      if (read_status(a) != 0) sm.stop = 1;
+      if (status != 0) sm.stop = 1;
       sm.ticket[s2] = nn;
       if (nn < a.n_tasks) stage_desc(a, nn, sm, s2);
     }
