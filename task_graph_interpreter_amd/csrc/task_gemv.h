@@ -178,6 +178,8 @@ __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t,
         if (lane == 0) sm.red[b] = norm ? 1.0f / sqrtf(ss / (float)K + eps) : 1.f;
       }
     }
+    // Trace mode: when the input was staged (mark 2; marks 0 and 1 are thread 0's).
+    if (a.trace != nullptr && lane == 0) sm.t_mark[2] = clock100();
   }
   __syncthreads();
   // Every wave now waits for its own ring and LDS prefetch.  Written as the builtin
