@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs into the traffic summary and exit")
     ap.add_argument("--pmc-command", default="", help="the profiled command, recorded in the summary")
-    ap.add_argument("--schedule", choices=["static", "dynamic"], default="static",
+    ap.add_argument("--schedule", choices=["static", "dynamic", "levels"], default="static",
                     help="how persistent workgroups find tasks: host-built lists or a ticket counter")
     args = ap.parse_args()
 
@@ -259,7 +259,7 @@ def main():
     scratch = torch.zeros(plan["scratch_bytes"], dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     g = mk.mk_build_graph(cfg, inp.weight_ptrs(), scratch.data_ptr(), stream)
-    modes = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC}
+    modes = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC, "levels": mk.MK_SCHED_LEVELS}
     g.mk_set_schedule(modes[args.schedule])
     tasks = g.tasks_bytes()
     n_nop = int((tasks[:, :2].copy().view(np.uint16)[:, 0] == 0).sum())  # op_id NOP = 0
@@ -313,13 +313,21 @@ def main():
 
     alt = None
     if not args.no_alt_schedule:
-        other = "dynamic" if args.schedule == "static" else "static"
-        g.mk_set_schedule(modes[other])
-        t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
-        assert g.mk_status() == 0
+        # The other schedule modes on the same graph: dynamic tickets, and the
+        # level-synchronous kernel (grid barrier between levels, no counters), each
+        # checked bitwise against the timed mode's logits first.
+        alt = []
+        ref_logits = inp.logits.clone()
+        for other in [m for m in modes if m != args.schedule]:
+            g.mk_set_schedule(modes[other])
+            g.mk_decode_step(stream, *ptrs)
+            assert g.mk_status() == 0
+            assert torch.equal(inp.logits, ref_logits), f"{other} schedule differs from {args.schedule}"
+            t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
+            assert g.mk_status() == 0
+            alt.append({"schedule": other, "ms_per_step": t_alt / args.steps})
+            log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
         g.mk_set_schedule(modes[args.schedule])
-        alt = {"schedule": other, "ms_per_step": t_alt / args.steps}
-        log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
 
     per_op = None
     if not args.no_per_op:
@@ -330,6 +338,23 @@ def main():
                   "latency_ms_median": float(np.median(per2)),
                   "speedup_of_persistent": ms2 / ms}
         log(f"per-op baseline: {ms2:.4f} ms/step")
+        # The same launches captured once into a HIP graph and replayed: no host cost
+        # per launch, one kernel boundary per op still.  Checked bitwise against the
+        # eager per-op step before it is timed.
+        g.mk_decode_step_per_op(stream, *ptrs)
+        torch.cuda.synchronize()
+        eager = inp.logits.clone()
+        g.mk_capture_per_op_graph(*ptrs)
+        inp.logits.zero_()
+        g.mk_launch_per_op_graph(stream)
+        assert g.mk_status() == 0
+        torch.cuda.synchronize()
+        assert torch.equal(inp.logits, eager), "graph replay of the per-op launches differs from the eager step"
+        t3, per3 = timed(lambda s, *p: g.mk_launch_per_op_graph(s), args.steps, args.warmup)
+        assert g.mk_status() == 0
+        per_op["graph_replay"] = {"ms_per_step": t3 / args.steps, "latency_ms_median": float(np.median(per3)),
+                                  "speedup_of_persistent": (t3 / args.steps) / ms}
+        log(f"per-op baseline, HIP graph replay: {t3 / args.steps:.4f} ms/step")
 
     if args.trace_out:
         tr = torch.zeros(plan["n_tasks"] * 8, dtype=torch.int64, device="cuda")

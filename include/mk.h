@@ -191,6 +191,18 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
                           const int32_t* positions_dev, void* kcache_dev, void* vcache_dev,
                           float* logits_dev);
 
+/* Context for the per-op baseline ("Megakernel iceberg" page, the CUDA-graphs layer:
+ * graph replay removes the host's per-launch cost but keeps one kernel boundary per
+ * op).  mk_capture_per_op_graph records the launches of mk_decode_step_per_op for
+ * the given step buffers into a HIP graph owned by `g` (replacing any earlier one),
+ * captured on a stream of the library's own; the buffers are baked into the graph and
+ * must stay valid while it is replayed.  mk_launch_per_op_graph enqueues one replay
+ * on `stream` (one whole step, same results as mk_decode_step_per_op).  Errors:
+ * MK_ERR_INVALID (bad arguments, or no graph captured yet), MK_ERR_HIP. */
+int mk_capture_per_op_graph(mk_graph* g, const int32_t* tokens_dev, const int32_t* positions_dev,
+                            void* kcache_dev, void* vcache_dev, float* logits_dev);
+int mk_launch_per_op_graph(mk_graph* g, void* stream);
+
 /* Synchronises `g`'s last stream and reads the device status word (see
  * MK_STATUS_*).  A non-zero status is cleared and the graph's scheduler state is
  * reset, so the next step runs normally.  Returns MK_ERR_DEVICE if it was non-zero. */
@@ -205,7 +217,8 @@ int mk_set_wait_limit(mk_graph* g, uint64_t ticks);
  * next mk_decode_step calls record per task {XCC_ID << 32 | HW_ID register, start
  * time, ready time (dependency wait over), body end time, release end time, mark 0,
  * mark 1, mark 2}, times in ticks of the constant 100 MHz clock.  Marks are points
- * inside a body (0 where a body sets none): GEMV -- input staged, last row reduced;
+ * inside a body (0 where a body sets none): GEMV -- every wave past the input
+ * staging, last row reduced, the control wave done staging the input;
  * ATTENTION_PARTIAL -- chunk folded, partials merged; ATTENTION_COMBINE -- weights
  * computed.  NOP joins run no body and record nothing.  NULL turns it off.  The
  * pointer must stay valid while steps that use it run. */
@@ -232,11 +245,17 @@ const char* mk_graph_kernel_name(const mk_graph* g);
  * MK_SCHED_DYNAMIC: each workgroup claims the next task index from a device-wide
  * ticket counter ("Megakernels", runhoid.com, Fig. 5 b: a queue the SMs pop from).
  *
- * In both modes NOP joins are never run as tasks: the parent whose arrival completes a
- * NOP's count counts the arrivals on the NOP's dependents itself.  Takes effect from
- * the next mk_decode_step; results are bitwise identical in both modes. */
+ * MK_SCHED_LEVELS: the level-synchronous variant of "Mega kernel initial" (1y33.com,
+ * the level section): the non-NOP tasks grouped by their level in the DAG, each level
+ * run round robin by the workgroups of one cooperative kernel, with a grid barrier
+ * between levels and no readiness counters.  An ablation of what the counters buy.
+ *
+ * In the counter modes NOP joins are never run as tasks: their children poll the
+ * join's own counter.  Takes effect from the next mk_decode_step; results are bitwise
+ * identical in all modes. */
 #define MK_SCHED_STATIC 0
 #define MK_SCHED_DYNAMIC 1
+#define MK_SCHED_LEVELS 2
 int mk_set_schedule(mk_graph* g, int mode);
 
 /* The static schedule: `order` holds the non-NOP task indices grouped by workgroup,

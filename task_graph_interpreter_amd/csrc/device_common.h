@@ -38,9 +38,10 @@ constexpr uint64_t kTagShift = 56;
 constexpr uint64_t kOffMask = (uint64_t(1) << kTagShift) - 1;
 
 struct Ctrl {
-  uint32_t head;    // ticket counter (monotone across steps)
-  uint32_t status;  // sticky device status word
-  uint32_t pad[62];
+  uint32_t head;     // ticket counter (monotone across steps)
+  uint32_t status;   // sticky device status word
+  uint32_t barrier;  // level-synchronous mode: grid-barrier arrivals (monotone across steps)
+  uint32_t pad[61];
 };
 
 struct Smem {
@@ -71,6 +72,10 @@ struct LaunchArgs {
   uint32_t ticket_base;
   uint32_t first_task;  // per-op launches: first task of the op
   uint64_t wait_limit;  // ticks of the 100 MHz clock
+  const uint32_t* lvl;       // level-synchronous mode: non-NOP task indices grouped by level
+  const uint32_t* lvl_off;   // [n_levels + 1]
+  uint32_t n_levels;         // non-empty levels
+  uint32_t barrier_base;     // Ctrl::barrier at the start of this step
   float rms_eps, rope_theta;
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, batch, intermediate, vocab, kv_capacity;
 };

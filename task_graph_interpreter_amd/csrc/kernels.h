@@ -233,14 +233,53 @@ __global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
   run_task_spec<S>(a, d, t, sm, false, nullptr);
 }
 
+// Level-synchronous variant ("Mega kernel initial", 1y33.com, the level section: the
+// host groups task indices by level and a grid barrier separates the levels), with the
+// same task bodies.  Every workgroup runs its round-robin share of a level, then all
+// meet at a device-wide barrier before the next level.  No readiness counters: every
+// parent of a task sits in an earlier level.  The barrier counts arrivals on one
+// monotone counter in the control block (target barrier_base + (level + 1) * grid, so
+// it needs no reset) after each workgroup's stores are acknowledged, and polls it with
+// the bounded wait of a dependency (a timeout reports task index 0x0FFFFFFF).
+template <class S>
+__global__ __launch_bounds__(kThreads, 1) void level_kernel(LaunchArgs a) {
+  __shared__ Smem sm;
+  const uint32_t G = gridDim.x;
+  for (uint32_t lv = 0; lv < a.n_levels; ++lv) {
+    const uint32_t b = ldg<uint32_t>(a.lvl_off, lv), e = ldg<uint32_t>(a.lvl_off, lv + 1);
+    for (uint32_t i = b + blockIdx.x; i < e; i += G) {
+      const uint32_t t = ldg<uint32_t>(a.lvl, i);
+      if (threadIdx.x == 0) stage_desc(a, t, sm, 0);
+      __syncthreads();
+      mk_task_t d = read_desc(sm, 0);
+      d.remaining_deps = 0;
+      run_task_spec<S>(a, d, t, sm, false, nullptr);
+      // Every wave's loads (LDS copies included) have landed and every wave is done
+      // with the LDS before the next descriptor is staged.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's stores acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      MK_GLOBAL uint32_t* bar = (MK_GLOBAL uint32_t*)&a.ctrl->barrier;
+      __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.flag = poll_counter(a, 0x0FFFFFFFu, (const uint32_t*)&a.ctrl->barrier, a.barrier_base + (lv + 1) * G);
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(sm.flag) == 0) break;  // step abandoned
+  }
+}
+
 struct KernelSet {
   const void* persistent;
   const void* per_op;
+  const void* levels;
 };
 
 template <class S>
 KernelSet kernel_set() {
-  return KernelSet{(const void*)interpreter_kernel<S>, (const void*)per_op_kernel<S>};
+  return KernelSet{(const void*)interpreter_kernel<S>, (const void*)per_op_kernel<S>, (const void*)level_kernel<S>};
 }
 
 }  // namespace mk

@@ -4,6 +4,7 @@
 // launch per op of the same task bodies (mk_decode_step_per_op, the baseline).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -18,6 +19,7 @@ namespace mk {
 struct KernelSet {
   const void* persistent;
   const void* per_op;
+  const void* levels;
 };
 
 // Specialisations compiled from kern_spec.hip, one object each.
@@ -76,6 +78,10 @@ struct mk_graph {
   uint32_t* d_join = nullptr;        // per task: its NOP join parent, or 0xFFFFFFFF
   uint32_t* d_order = nullptr;       // static schedule lists
   uint32_t* d_order_off = nullptr;   // [grid + 1]
+  uint32_t* d_lvl = nullptr;         // level-synchronous lists: non-NOP tasks by level
+  uint32_t* d_lvl_off = nullptr;     // [n_lvls + 1]
+  uint32_t n_lvls = 0;               // non-empty levels
+  uint32_t barrier_base = 0;         // Ctrl::barrier before the next level-synchronous step
   float* d_rope = nullptr;           // [kv_capacity][head_dim / 2] (cos, sin) pairs
   mk::Schedule sched;
   int sched_mode = MK_SCHED_STATIC;
@@ -86,6 +92,8 @@ struct mk_graph {
   uint32_t epoch = 0;
   uint32_t ticket_base = 0;
   uint64_t wait_limit = 200000000ull;
+  hipGraph_t per_op_graph = nullptr;        // captured per-op launches (baseline context)
+  hipGraphExec_t per_op_exec = nullptr;
   bool needs_reset = false;
   hipStream_t last_stream = nullptr;
 };
@@ -137,6 +145,10 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   a.rt[mk::TAG_LOGITS] = (uint64_t)(uintptr_t)logits;
   a.n_tasks = (uint32_t)g->low.tasks.size();
   a.wait_limit = g->wait_limit;
+  a.lvl = g->d_lvl;
+  a.lvl_off = g->d_lvl_off;
+  a.n_levels = g->n_lvls;
+  a.barrier_base = g->barrier_base;
   const mk_model_cfg& c = g->low.cfg;
   a.rms_eps = c.rms_eps;
   a.rope_theta = c.rope_theta;
@@ -173,6 +185,7 @@ int reset_state(mk_graph* g, hipStream_t s) {
   HIP_TRY(hipGetLastError());
   g->epoch = 0;
   g->ticket_base = 0;
+  g->barrier_base = 0;
   g->needs_reset = false;
   return MK_OK;
 }
@@ -284,7 +297,32 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   // evaluating binary64 transcendentals on the critical path.
   const size_t half = (size_t)L.cfg.head_dim / 2, cap = (size_t)L.cfg.kv_capacity;
   const size_t off_rope = (off_order_off + S.offsets.size() * 4 + 15) & ~(size_t)15;
-  const size_t blob_bytes = off_rope + cap * half * 8;
+  // Level-synchronous lists: the level of a task is one more than its parents' highest
+  // (tasks are in topological order, so one forward pass over the dependents lists
+  // settles every level); the non-NOP tasks grouped by level, ascending within a
+  // level, and levels holding only NOP joins dropped.
+  std::vector<uint32_t> level(nt, 0);
+  uint32_t max_level = 0;
+  for (size_t t = 0; t < nt; ++t) {
+    const mk_task_t& d = L.tasks[t];
+    max_level = std::max(max_level, level[t]);
+    for (int32_t i = 0; i < d.num_dependents; ++i) {
+      const uint32_t c = L.edges[(size_t)d.dependents_offset + i];
+      level[c] = std::max(level[c], level[t] + 1);
+    }
+  }
+  std::vector<std::vector<uint32_t>> by_level(nt ? max_level + 1 : 0);
+  for (size_t t = 0; t < nt; ++t)
+    if (L.tasks[t].op_id != MK_OP_NOP) by_level[level[t]].push_back((uint32_t)t);
+  std::vector<uint32_t> lvl, lvl_off{0};
+  for (const auto& v : by_level) {
+    if (v.empty()) continue;
+    lvl.insert(lvl.end(), v.begin(), v.end());
+    lvl_off.push_back((uint32_t)lvl.size());
+  }
+  const size_t off_lvl = off_rope + cap * half * 8;
+  const size_t off_lvl_off = off_lvl + lvl.size() * 4;
+  const size_t blob_bytes = off_lvl_off + lvl_off.size() * 4;
   std::vector<char> blob(blob_bytes);
   {
     float* rope = (float*)(blob.data() + off_rope);
@@ -303,6 +341,8 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   if (nt) std::memcpy(blob.data() + off_join, join.data(), nt * 4);
   if (no) std::memcpy(blob.data() + off_order, S.order.data(), no * 4);
   std::memcpy(blob.data() + off_order_off, S.offsets.data(), S.offsets.size() * 4);
+  if (!lvl.empty()) std::memcpy(blob.data() + off_lvl, lvl.data(), lvl.size() * 4);
+  std::memcpy(blob.data() + off_lvl_off, lvl_off.data(), lvl_off.size() * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
   if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
   if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4 * (size_t)mk::kArrivalStride)) != hipSuccess)
@@ -314,6 +354,9 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   g->d_order = (uint32_t*)(g->d_blob + off_order);
   g->d_order_off = (uint32_t*)(g->d_blob + off_order_off);
   g->d_rope = (float*)(g->d_blob + off_rope);
+  g->d_lvl = (uint32_t*)(g->d_blob + off_lvl);
+  g->d_lvl_off = (uint32_t*)(g->d_blob + off_lvl_off);
+  g->n_lvls = (uint32_t)(lvl_off.size() - 1);
   if ((e = hipMemcpyAsync(g->d_blob, blob.data(), blob_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     return fail(hip_fail(e, "hipMemcpyAsync(blob)"));
   if ((e = hipMemcpyAsync(g->d_table, table.data(), table.size() * 8, hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -348,7 +391,7 @@ int mk_graph_grid(const mk_graph* g, uint32_t* workgroups) {
 const char* mk_graph_kernel_name(const mk_graph* g) { return g && g->spec ? g->spec->name : ""; }
 
 int mk_set_schedule(mk_graph* g, int mode) {
-  if (!g || (mode != MK_SCHED_STATIC && mode != MK_SCHED_DYNAMIC))
+  if (!g || (mode != MK_SCHED_STATIC && mode != MK_SCHED_DYNAMIC && mode != MK_SCHED_LEVELS))
     return mk::set_error(MK_ERR_INVALID, "graph is NULL or unknown schedule mode");
   g->sched_mode = mode;
   return MK_OK;
@@ -387,6 +430,14 @@ int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const i
   a.epoch = g->epoch + 1;
   a.ticket_base = g->ticket_base;
   void* params[] = {&a};
+  if (g->sched_mode == MK_SCHED_LEVELS) {
+    // Counters untouched (the epoch stays): only the barrier counter advances.
+    hipError_t e = hipLaunchCooperativeKernel(g->kernels.levels, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(levels)");
+    g->barrier_base += g->n_lvls * g->grid;
+    g->last_stream = s;
+    return MK_OK;
+  }
   // Cooperative launch: the runtime refuses the launch (instead of letting the
   // spinning workgroups deadlock) if the whole grid cannot be resident at once.
   hipError_t e = hipLaunchCooperativeKernel(g->kernels.persistent, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
@@ -415,6 +466,58 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev, 
   return MK_OK;
 }
 
+namespace {
+
+void drop_per_op_graph(mk_graph* g) {
+  if (g->per_op_exec) (void)hipGraphExecDestroy(g->per_op_exec);
+  if (g->per_op_graph) (void)hipGraphDestroy(g->per_op_graph);
+  g->per_op_exec = nullptr;
+  g->per_op_graph = nullptr;
+}
+
+}  // namespace
+
+int mk_capture_per_op_graph(mk_graph* g, const int32_t* tokens_dev, const int32_t* positions_dev,
+                            void* kcache_dev, void* vcache_dev, float* logits_dev) {
+  int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  if (rc) return rc;
+  drop_per_op_graph(g);
+  hipStream_t cs = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+    a.trace = nullptr;
+    for (const mk::OpRange& op : g->low.ops) {
+      a.first_task = op.first;
+      void* params[] = {&a};
+      e = hipLaunchKernel(g->kernels.per_op, dim3(op.count), dim3(mk::kThreads), params, 0, cs);
+      if (e != hipSuccess) break;
+    }
+    hipGraph_t graph = nullptr;
+    const hipError_t e2 = hipStreamEndCapture(cs, &graph);  // ends the capture on every path
+    if (e == hipSuccess) e = e2;
+    if (e == hipSuccess) e = hipGraphInstantiate(&g->per_op_exec, graph, nullptr, nullptr, 0);
+    if (e == hipSuccess) g->per_op_graph = graph;
+    else if (graph) (void)hipGraphDestroy(graph);
+  }
+  (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) {
+    g->per_op_exec = nullptr;
+    return hip_fail(e, "capturing the per-op launches");
+  }
+  return MK_OK;
+}
+
+int mk_launch_per_op_graph(mk_graph* g, void* stream) {
+  if (!g) return mk::set_error(MK_ERR_INVALID, "NULL graph");
+  if (!g->per_op_exec) return mk::set_error(MK_ERR_INVALID, "no per-op graph captured");
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipGraphLaunch(g->per_op_exec, s));
+  g->last_stream = s;
+  return MK_OK;
+}
+
 int mk_status(mk_graph* g, uint32_t* device_status) {
   if (!g || !device_status) return mk::set_error(MK_ERR_INVALID, "NULL argument");
   HIP_TRY(hipStreamSynchronize(g->last_stream));
@@ -432,6 +535,7 @@ int mk_status(mk_graph* g, uint32_t* device_status) {
 
 void mk_destroy(mk_graph* g) {
   if (!g) return;
+  drop_per_op_graph(g);
   if (g->last_stream) (void)hipStreamSynchronize(g->last_stream);
   free_graph(g);
 }

@@ -64,19 +64,36 @@ def test_tiny_step_all_activations(path):
     run.close()
 
 
-SCHED = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC}
+SCHED = {"static": mk.MK_SCHED_STATIC, "dynamic": mk.MK_SCHED_DYNAMIC, "levels": mk.MK_SCHED_LEVELS}
 
 
 def test_persistent_equals_per_op_bitwise_and_is_repeatable():
     w = workloads.tiny()
-    _say("tiny persistent (static and dynamic lists) vs per-op bitwise, 5 repeats each")
+    _say("tiny persistent (static and dynamic lists, level-synchronous) vs per-op bitwise, 5 repeats each")
     run = MkRun(w)
     a = run.step("per_op")
-    for mode in ["static", "dynamic", "static"]:
+    for mode in ["static", "dynamic", "levels", "static", "levels"]:
         run.graph.mk_set_schedule(SCHED[mode])
         for _ in range(5):
             b = run.step("persistent")
             assert np.array_equal(a, b), mode
+    run.close()
+
+
+def test_per_op_graph_replays_equal_eager_per_op():
+    w = workloads.tiny()
+    _say("tiny per-op launches captured in a HIP graph: 4 replays vs eager per-op, bitwise")
+    run = MkRun(w)
+    ref = run.step("per_op")
+    run.graph.mk_capture_per_op_graph(*run.inp.step_ptrs())
+    for i in range(4):
+        run.inp.logits.zero_()  # eager work on the same buffers between replays
+        run.graph.mk_launch_per_op_graph(run.stream)
+        assert run.graph.mk_status() == 0
+        torch.cuda.synchronize()
+        got = run.inp.logits.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), f"replay {i}"
+        assert np.array_equal(run.step("per_op"), ref), f"eager step after replay {i}"
     run.close()
 
 
@@ -91,7 +108,7 @@ def test_device_schedule_equals_host_schedule():
     run.close()
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", ["static", "dynamic", "levels"])
 @pytest.mark.parametrize("joins", [1, 0])
 def test_tiny_variants_bf16_batch_ragged(joins, mode):
     # bf16 weights and cache, 3 sequences of different lengths, GQA 8/2, tiles and
@@ -218,7 +235,7 @@ def test_bad_token_reports_status_then_recovers(bad):
     run.close()
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", ["static", "dynamic", "levels"])
 def test_wait_timeout_drains_and_recovers(mode):
     # A 1-tick bound on every dependency wait: tasks whose producers are not done at
     # the first look give up, the step drains, mk_status reports a timeout, and the
