@@ -162,8 +162,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
 def greedy_run(w, inp, n_tokens, stream):
     """Greedy decode of n_tokens tokens from the timed step's position onward, with a
     graph lowered for n_tokens more cache slots on the same weights.  The loop never
-    touches the host: argmax (lowest index on ties) and the position update run on the
-    device between steps.  Returns time between tokens."""
+    touches the host: mk_decode_greedy enqueues every step followed by the library's
+    SAMPLE kernel (argmax, lowest index on ties, and the position update).  Returns
+    time between tokens."""
     import torch
 
     import task_graph_interpreter_amd as mk
@@ -179,22 +180,21 @@ def greedy_run(w, inp, n_tokens, stream):
     ptrs2 = inp2.step_ptrs()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = torch.empty(n_tokens * w.batch, dtype=torch.int32, device="cuda")
     ev0.record()
-    for _ in range(n_tokens):
-        g2.mk_decode_step(stream, *ptrs2)
-        inp2.tokens.copy_(torch.argmax(inp2.logits, dim=-1).to(torch.int32))
-        inp2.positions.add_(1)
+    g2.mk_decode_greedy(stream, n_tokens, *ptrs2, out.data_ptr())
     ev1.record()
     torch.cuda.synchronize()
     assert g2.mk_status() == 0
+    assert int(inp2.positions[0]) == int(w.positions()[0]) + n_tokens
     total = ev0.elapsed_time(ev1)
     g2.close()
     del keep2
     log(f"greedy: {n_tokens} tokens, {total / n_tokens:.4f} ms between tokens")
     return {"tokens": n_tokens, "ms_per_token": total / n_tokens, "tokens_per_s": w.batch * n_tokens / (total / 1e3),
             "first_position": int(w.positions()[0]), "kv_slots": w2.kv_capacity,
-            "note": "graph lowered for kv_len + tokens (empty chunks until reached); argmax and position "
-                    "update on the device between steps"}
+            "note": "graph lowered for kv_len + tokens (empty chunks until reached); mk_decode_greedy: "
+                    "each step followed by the SAMPLE kernel (argmax and position update), no host round trip"}
 
 
 def main():

@@ -191,6 +191,26 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
                           const int32_t* positions_dev, void* kcache_dev, void* vcache_dev,
                           float* logits_dev);
 
+/* Greedy SAMPLE ("Mega kernel initial", 1y33.com, the op table: SAMPLE), enqueued on
+ * `stream` (no host synchronisation): for each batch row b, tokens_dev[b] = the lowest
+ * index holding the largest value of logits_dev row b ([batch, vocab] fp32; NaN never
+ * wins, a row with no comparable value gives 0), and positions_dev[b] += 1, ready
+ * for the next step.  One workgroup per row; batch and vocab are the graph's.  Runs as
+ * its own small kernel after the step rather than as tasks of the graph.  Errors:
+ * MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP. */
+int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t* tokens_dev,
+                     int32_t* positions_dev);
+
+/* n_steps greedy decode steps with no host round trip: each is mk_decode_step on these
+ * buffers followed by mk_sample_greedy, so step i + 1 embeds step i's tokens at the
+ * next positions and appends to the same caches.  When tokens_out_dev is non-NULL
+ * (device, n_steps * batch int32), step i's tokens are also written to
+ * tokens_out_dev[i * batch + b].  Positions must stay below each sequence's kv_len
+ * (the graph's chunk fan-out); a step past it sets MK_STATUS_BAD_POSITION, which
+ * mk_status reports.  Same errors as mk_decode_step. */
+int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev, int32_t* positions_dev,
+                     void* kcache_dev, void* vcache_dev, float* logits_dev, int32_t* tokens_out_dev);
+
 /* Context for the per-op baseline ("Megakernel iceberg" page, the CUDA-graphs layer:
  * graph replay removes the host's per-launch cost but keeps one kernel boundary per
  * op).  mk_capture_per_op_graph records the launches of mk_decode_step_per_op for

@@ -39,7 +39,8 @@ MK_DTYPE = {"f32": 0, "bf16": 1}
 # Every symbol include/mk.h declares.
 EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
            "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
-           "mk_decode_step_per_op", "mk_capture_per_op_graph", "mk_launch_per_op_graph", "mk_status",
+           "mk_decode_step_per_op", "mk_sample_greedy", "mk_decode_greedy", "mk_capture_per_op_graph",
+           "mk_launch_per_op_graph", "mk_status",
            "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid", "mk_graph_kernel_name", "mk_set_schedule", "mk_graph_schedule", "mk_lowered_schedule", "mk_destroy", "mk_last_error", "mk_abi_version"]
 
 
@@ -102,6 +103,8 @@ def lib():
         "mk_graph_edges": ([vp, P(P(u32)), P(u32)], i32),
         "mk_decode_step": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "mk_decode_step_per_op": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "mk_sample_greedy": ([vp, vp, vp, vp, vp], i32),
+        "mk_decode_greedy": ([vp, vp, i32, vp, vp, vp, vp, vp, vp], i32),
         "mk_capture_per_op_graph": ([vp, vp, vp, vp, vp, vp], i32),
         "mk_launch_per_op_graph": ([vp, vp], i32),
         "mk_status": ([vp, P(u32)], i32),
@@ -231,6 +234,12 @@ class Graph:
 
     def mk_decode_step_per_op(self, stream, tokens, positions, kcache, vcache, logits) -> None:
         _check(lib().mk_decode_step_per_op(self.h, stream, tokens, positions, kcache, vcache, logits))
+
+    def mk_sample_greedy(self, stream, logits, tokens, positions) -> None:
+        _check(lib().mk_sample_greedy(self.h, stream, logits, tokens, positions))
+
+    def mk_decode_greedy(self, stream, n_steps, tokens, positions, kcache, vcache, logits, tokens_out=None) -> None:
+        _check(lib().mk_decode_greedy(self.h, stream, n_steps, tokens, positions, kcache, vcache, logits, tokens_out))
 
     def mk_capture_per_op_graph(self, tokens, positions, kcache, vcache, logits) -> None:
         _check(lib().mk_capture_per_op_graph(self.h, tokens, positions, kcache, vcache, logits))

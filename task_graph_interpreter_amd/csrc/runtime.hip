@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -56,6 +57,53 @@ static const SpecEntry* select_spec(const mk_model_cfg& c) {
     if (s.kba == 0 && s.kbd == 0) generic = &s;
   }
   return generic;
+}
+
+// Greedy SAMPLE ("Mega kernel initial", the op table's SAMPLE: argmax over the
+// vocabulary), one workgroup per batch row: tokens[b] = the lowest index holding the
+// row's largest logit (NaN never wins; a row with no comparable value gives 0), also
+// written to out[b] when out is non-null, and positions[b] += 1 for the next step.
+constexpr int kSampleThreads = 256;
+__global__ __launch_bounds__(kSampleThreads) void sample_greedy_kernel(const float* logits, int vocab,
+                                                                        int32_t* tokens, int32_t* positions,
+                                                                        int32_t* out) {
+  const int b = blockIdx.x;
+  const float* row = logits + (size_t)b * vocab;
+  float best = -INFINITY;
+  int bi = INT32_MAX;
+  for (int v = threadIdx.x; v < vocab; v += kSampleThreads) {
+    const float x = row[v];
+    if (x > best || (x == best && v < bi)) {
+      best = x;
+      bi = v;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ob > best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  __shared__ float sb[kSampleThreads / 64];
+  __shared__ int si[kSampleThreads / 64];
+  if ((threadIdx.x & 63) == 0) {
+    sb[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kSampleThreads / 64; ++w)
+      if (sb[w] > best || (sb[w] == best && si[w] < bi)) {
+        best = sb[w];
+        bi = si[w];
+      }
+    const int32_t tok = bi == INT32_MAX ? 0 : bi;
+    tokens[b] = tok;
+    if (out) out[b] = tok;
+    positions[b] += 1;
+  }
 }
 
 __global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
@@ -463,6 +511,37 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev, 
     HIP_TRY(hipLaunchKernel(g->kernels.per_op, dim3(op.count), dim3(mk::kThreads), params, 0, s));
   }
   g->last_stream = s;
+  return MK_OK;
+}
+
+int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t* tokens_dev,
+                     int32_t* positions_dev) {
+  if (!g || !logits_dev || !tokens_dev || !positions_dev) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  if (misaligned(logits_dev, 4) || misaligned(tokens_dev, 4) || misaligned(positions_dev, 4))
+    return mk::set_error(MK_ERR_ALIGN, "logits/tokens/positions must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const mk_model_cfg& c = g->low.cfg;
+  hipLaunchKernelGGL(mk::sample_greedy_kernel, dim3(c.batch), dim3(mk::kSampleThreads), 0, s, logits_dev, c.vocab,
+                     tokens_dev, positions_dev, (int32_t*)nullptr);
+  HIP_TRY(hipGetLastError());
+  g->last_stream = s;
+  return MK_OK;
+}
+
+int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev, int32_t* positions_dev,
+                     void* kcache_dev, void* vcache_dev, float* logits_dev, int32_t* tokens_out_dev) {
+  if (n_steps < 0) return mk::set_error(MK_ERR_INVALID, "n_steps < 0");
+  if (misaligned(tokens_out_dev, 4)) return mk::set_error(MK_ERR_ALIGN, "tokens_out must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int batch = g ? g->low.cfg.batch : 0;
+  for (int i = 0; i < n_steps; ++i) {
+    int rc = mk_decode_step(g, stream, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+    if (rc) return rc;
+    hipLaunchKernelGGL(mk::sample_greedy_kernel, dim3(batch), dim3(mk::kSampleThreads), 0, s, logits_dev,
+                       g->low.cfg.vocab, tokens_dev, positions_dev,
+                       tokens_out_dev ? tokens_out_dev + (size_t)i * batch : (int32_t*)nullptr);
+    HIP_TRY(hipGetLastError());
+  }
   return MK_OK;
 }
 

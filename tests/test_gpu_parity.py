@@ -201,6 +201,54 @@ def test_tiny_greedy_8_steps(path):
     run.close()
 
 
+def test_sample_greedy_lowest_index_on_ties():
+    w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1, batch=3,
+                                 kv_len=(128, 41, 97), n_q_heads=8, gemv_tiles=5, kv_chunk=24, name="tiny_bf16_b3")
+    _say("greedy SAMPLE kernel on crafted logits: ties, an all-equal row, a NaN")
+    run = MkRun(w)
+    rng = np.random.default_rng(7)
+    rows = rng.standard_normal((w.batch, w.vocab)).astype(np.float32)
+    rows[0, [900, 7, 513]] = 9.0            # tie: the lowest index wins
+    rows[1, :] = -2.5                        # every entry equal: index 0
+    rows[2, 11] = np.nan                     # NaN never wins
+    rows[2, 700] = 8.0
+    logits = torch.from_numpy(rows).cuda()
+    tokens = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda")
+    positions = torch.tensor([5, 40, 96], dtype=torch.int32, device="cuda")
+    run.graph.mk_sample_greedy(run.stream, logits.data_ptr(), tokens.data_ptr(), positions.data_ptr())
+    torch.cuda.synchronize()
+    assert tokens.cpu().tolist() == [7, 0, 700]
+    assert tokens.cpu().tolist()[2] == int(np.nanargmax(rows[2]))
+    assert positions.cpu().tolist() == [6, 41, 97]
+    run.close()
+
+
+def test_device_greedy_loop_8_steps():
+    w = workloads.tiny().with_steps(8)
+    _say("tiny 8 greedy steps on the device (decode step + SAMPLE kernel, no host round trip)")
+    run = MkRun(w)
+    p = GeneratedParams(w)
+    kv = od.KVState(p)
+    tok = w.tokens()
+    pos = workloads.tiny().positions()
+    run.inp.set_step(tok, pos)
+    out = torch.full((8 * w.batch,), -1, dtype=torch.int32, device="cuda")
+    run.graph.mk_decode_greedy(run.stream, 8, *run.inp.step_ptrs(), out.data_ptr())
+    assert run.graph.mk_status() == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(8, w.batch)
+    for s in range(8):
+        ref, _ = od.decode_step(w, p, tok, pos, kv)
+        t_ref = od.greedy_token(ref[0])
+        assert got[s, 0] == t_ref, (s, int(got[s, 0]), t_ref, od.top2_margin(ref[0]))
+        tok = np.array([t_ref], dtype=np.int32)
+        pos = pos + 1
+    check_close(run.inp.logits.cpu().numpy().astype(np.float64), ref, "logits of the last step")
+    assert run.inp.tokens.cpu().tolist() == [int(got[7, 0])]
+    assert run.inp.positions.cpu().tolist() == pos.tolist()
+    run.close()
+
+
 def test_bad_position_reports_status_then_recovers():
     w = workloads.tiny()
     _say("tiny bad position status")
