@@ -174,6 +174,11 @@ def llama1b() -> Workload:
                     gemv_tiles=256, kv_chunk=128, kv_len=(1024,), kv_capacity=1024, gemv_config=1)
 
 
+def llama1b_kv512() -> Workload:
+    # The first page's measured point: 1B-class decoder, 512 cached tokens, greedy decode.
+    return llama1b().replace(name="1b_b1_kv512", kv_len=(512,), kv_capacity=512)
+
+
 def llama8b() -> Workload:
     return Workload(name="8b_b1", n_layers=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
                     intermediate=14336, vocab=128256, batch=1, weight_dtype="bf16", kv_dtype="bf16",
@@ -194,6 +199,7 @@ def llama8b_long() -> Workload:
 WORKLOADS = {
     "tiny": tiny,
     "1b_b1": llama1b,
+    "1b_b1_kv512": llama1b_kv512,
     "8b_b1": llama8b,
     "8b_b8_ragged": llama8b_ragged,
     "8b_b32_32k": llama8b_long,
