@@ -97,16 +97,22 @@ def cpu_baseline(w, budget_layers=(1, 2), min_seconds=6.0):
 KERNEL_SRC = os.path.join(ROOT, "task_graph_interpreter_amd", "csrc")
 
 
+# The sources the persistent kernel is compiled from (kern_spec.hip and what it
+# includes, the specialisation list, and the ABI header that fixes the descriptor
+# layout); host-only files (lowering, scheduling, runtime) do not change it.
+KERNEL_FILES = ["kern_spec.hip", "kernels.h", "tasks.h", "task_gemv.h", "task_gemv_mfma.h", "task_attn.h",
+                "device_common.h", "specs.def", os.path.join("..", "..", "include", "mk.h")]
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP kernel sources: a traffic figure taken from hardware counters
-    is only reported while the kernels are the ones it was measured on."""
+    """Hash of the persistent kernel's sources: a traffic figure taken from hardware
+    counters is only reported while the kernel is the one it was measured on."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SRC)):
-        if name.endswith((".h", ".hip", ".cpp", ".def")):
-            h.update(name.encode())
-            with open(os.path.join(KERNEL_SRC, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_FILES:
+        h.update(os.path.basename(name).encode())
+        with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

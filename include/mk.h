@@ -162,6 +162,12 @@ int mk_lowered_scratch_span(const mk_lowered* g, uint32_t buf_index, uint64_t* o
  * owned by the mk_lowered object and replaced by the next call. */
 int mk_lowered_schedule(mk_lowered* g, uint32_t workers, const uint32_t** order,
                         const uint32_t** offsets, double* est_us);
+/* Level-synchronous lists (the order MK_SCHED_LEVELS runs): the non-NOP task indices
+ * grouped by level of the task DAG (one more than the highest level among a task's
+ * parents, NOP joins included in that count), ascending within a level, levels that
+ * hold only NOP joins dropped.  Level i is tasks[offsets[i] .. offsets[i + 1]), i <
+ * n_levels.  Arrays are library-owned, valid until the next call or mk_lowered_free. */
+int mk_lowered_levels(mk_lowered* g, const uint32_t** tasks, const uint32_t** offsets, uint32_t* n_levels);
 void mk_lowered_free(mk_lowered* g);
 
 /* Lower, then upload descriptors + edges (one blob behind a 64-byte header) and the

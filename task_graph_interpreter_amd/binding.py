@@ -38,7 +38,7 @@ MK_DTYPE = {"f32": 0, "bf16": 1}
 
 # Every symbol include/mk.h declares.
 EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
-           "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
+           "mk_lowered_levels", "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
            "mk_decode_step_per_op", "mk_sample_greedy", "mk_decode_greedy", "mk_capture_per_op_graph",
            "mk_launch_per_op_graph", "mk_status",
            "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid", "mk_graph_kernel_name", "mk_set_schedule", "mk_graph_schedule", "mk_lowered_schedule", "mk_destroy", "mk_last_error", "mk_abi_version"]
@@ -97,6 +97,7 @@ def lib():
         "mk_lowered_tasks": ([vp, P(P(MkTask)), P(u32)], i32),
         "mk_lowered_edges": ([vp, P(P(u32)), P(u32)], i32),
         "mk_lowered_scratch_span": ([vp, u32, P(u64), P(u64)], i32),
+        "mk_lowered_levels": ([vp, P(P(u32)), P(P(u32)), P(u32)], i32),
         "mk_lowered_free": ([vp], None),
         "mk_build_graph": ([P(MkModelCfg), P(MkWeights), vp, vp, P(vp)], i32),
         "mk_graph_tasks": ([vp, P(P(MkTask)), P(u32)], i32),
@@ -201,6 +202,14 @@ class Lowered:
         o, f, est = ctypes.POINTER(ctypes.c_uint32)(), ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_double()
         _check(lib().mk_lowered_schedule(self.h, workers, ctypes.byref(o), ctypes.byref(f), ctypes.byref(est)))
         return _schedule_to_numpy(o, f, workers), est.value
+
+    def levels(self):
+        """Level-synchronous lists: a list of int arrays, one per level, in run order."""
+        t, f, n = ctypes.POINTER(ctypes.c_uint32)(), ctypes.POINTER(ctypes.c_uint32)(), ctypes.c_uint32()
+        _check(lib().mk_lowered_levels(self.h, ctypes.byref(t), ctypes.byref(f), ctypes.byref(n)))
+        offs = np.ctypeslib.as_array(f, shape=(n.value + 1,)).copy()
+        tasks = np.ctypeslib.as_array(t, shape=(int(offs[-1]),)).copy() if offs[-1] else np.zeros(0, np.uint32)
+        return [tasks[offs[i]:offs[i + 1]] for i in range(n.value)]
 
     def scratch_span(self, buf_index: int):
         off, nb = ctypes.c_uint64(), ctypes.c_uint64()

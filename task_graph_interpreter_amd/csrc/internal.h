@@ -82,6 +82,13 @@ struct Schedule {
 };
 void build_schedule(const Lowered& L, uint32_t workers, Schedule& out);
 
+// Level-synchronous lists: the non-NOP tasks grouped by their level in the DAG.
+struct Levels {
+  std::vector<uint32_t> tasks;    // task indices, grouped by level, ascending within one
+  std::vector<uint32_t> offsets;  // [levels + 1]
+};
+void build_levels(const Lowered& L, Levels& out);
+
 int set_error(int code, const std::string& msg);
 
 }  // namespace mk
@@ -89,4 +96,5 @@ int set_error(int code, const std::string& msg);
 struct mk_lowered {
   mk::Lowered low;
   mk::Schedule sched;
+  mk::Levels levels;
 };

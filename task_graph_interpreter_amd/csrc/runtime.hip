@@ -345,29 +345,10 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   // evaluating binary64 transcendentals on the critical path.
   const size_t half = (size_t)L.cfg.head_dim / 2, cap = (size_t)L.cfg.kv_capacity;
   const size_t off_rope = (off_order_off + S.offsets.size() * 4 + 15) & ~(size_t)15;
-  // Level-synchronous lists: the level of a task is one more than its parents' highest
-  // (tasks are in topological order, so one forward pass over the dependents lists
-  // settles every level); the non-NOP tasks grouped by level, ascending within a
-  // level, and levels holding only NOP joins dropped.
-  std::vector<uint32_t> level(nt, 0);
-  uint32_t max_level = 0;
-  for (size_t t = 0; t < nt; ++t) {
-    const mk_task_t& d = L.tasks[t];
-    max_level = std::max(max_level, level[t]);
-    for (int32_t i = 0; i < d.num_dependents; ++i) {
-      const uint32_t c = L.edges[(size_t)d.dependents_offset + i];
-      level[c] = std::max(level[c], level[t] + 1);
-    }
-  }
-  std::vector<std::vector<uint32_t>> by_level(nt ? max_level + 1 : 0);
-  for (size_t t = 0; t < nt; ++t)
-    if (L.tasks[t].op_id != MK_OP_NOP) by_level[level[t]].push_back((uint32_t)t);
-  std::vector<uint32_t> lvl, lvl_off{0};
-  for (const auto& v : by_level) {
-    if (v.empty()) continue;
-    lvl.insert(lvl.end(), v.begin(), v.end());
-    lvl_off.push_back((uint32_t)lvl.size());
-  }
+  mk::Levels levels;
+  mk::build_levels(L, levels);
+  const std::vector<uint32_t>& lvl = levels.tasks;
+  const std::vector<uint32_t>& lvl_off = levels.offsets;
   const size_t off_lvl = off_rope + cap * half * 8;
   const size_t off_lvl_off = off_lvl + lvl.size() * 4;
   const size_t blob_bytes = off_lvl_off + lvl_off.size() * 4;

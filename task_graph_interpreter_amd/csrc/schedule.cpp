@@ -85,6 +85,53 @@ void build_schedule(const Lowered& L, uint32_t workers, Schedule& S) {
 
 }  // namespace mk
 
+namespace mk {
+
+// Level-synchronous lists: the level of a task is one more than its parents' highest
+// (tasks are in topological order, so one forward pass over the dependents lists
+// settles every level); the non-NOP tasks grouped by level, ascending within a level,
+// and levels holding only NOP joins dropped.  Level i is tasks[offsets[i] ..
+// offsets[i + 1]).
+void build_levels(const Lowered& L, Levels& out) {
+  const size_t nt = L.tasks.size();
+  std::vector<uint32_t> level(nt, 0);
+  uint32_t max_level = 0;
+  for (size_t t = 0; t < nt; ++t) {
+    const mk_task_t& d = L.tasks[t];
+    max_level = std::max(max_level, level[t]);
+    for (int32_t i = 0; i < d.num_dependents; ++i) {
+      const uint32_t c = L.edges[(size_t)d.dependents_offset + i];
+      level[c] = std::max(level[c], level[t] + 1);
+    }
+  }
+  std::vector<std::vector<uint32_t>> by_level(nt ? max_level + 1 : 0);
+  for (size_t t = 0; t < nt; ++t)
+    if (L.tasks[t].op_id != MK_OP_NOP) by_level[level[t]].push_back((uint32_t)t);
+  out.tasks.clear();
+  out.offsets.assign(1, 0);
+  for (const auto& v : by_level) {
+    if (v.empty()) continue;
+    out.tasks.insert(out.tasks.end(), v.begin(), v.end());
+    out.offsets.push_back((uint32_t)out.tasks.size());
+  }
+}
+
+}  // namespace mk
+
+extern "C" int mk_lowered_levels(mk_lowered* g, const uint32_t** tasks, const uint32_t** offsets,
+                                 uint32_t* n_levels) {
+  if (!g || !tasks || !offsets || !n_levels) return mk::set_error(MK_ERR_INVALID, "NULL argument");
+  try {
+    mk::build_levels(g->low, g->levels);
+  } catch (const std::bad_alloc&) {
+    return mk::set_error(MK_ERR_NOMEM, "out of host memory while grouping levels");
+  }
+  *tasks = g->levels.tasks.data();
+  *offsets = g->levels.offsets.data();
+  *n_levels = (uint32_t)(g->levels.offsets.size() - 1);
+  return MK_OK;
+}
+
 extern "C" int mk_lowered_schedule(mk_lowered* g, uint32_t workers, const uint32_t** order,
                                    const uint32_t** offsets, double* est_us) {
   if (!g || !order || !offsets || workers == 0) return mk::set_error(MK_ERR_INVALID, "NULL argument or 0 workers");
