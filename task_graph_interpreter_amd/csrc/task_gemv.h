@@ -113,8 +113,8 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
 }
 
 // Wait for the tile's producers and stage its input rows 0 .. nb-1 (x * gamma with
-// RMS_NORM_INPUT) into LDS, both on the control wave alone, then meet the other waves
-// at one barrier; returns r_b (1 without the norm) in rs[], or false if the step was
+// RMS_NORM_INPUT) into LDS, both on the control wave alone (spread: the copies are
+// shared by every wave, see below), then meet the other waves at one barrier; returns r_b (1 without the norm) in rs[], or false if the step was
 // abandoned.  The control wave has issued no LDS prefetch, so its poll and its staging
 // loads queue only behind its own weight ring, not behind the tile's bulk prefetch,
 // which keeps arriving meanwhile.  The input rows are copied into LDS by device-scope
@@ -124,62 +124,71 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
 template <int BM, bool GBF16>
 __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t, int32_t indeg, const float* x,
                                                 const char* gamma, bool norm, int K, int nb, float eps, Smem& sm,
-                                                float rs[BM]) {
-  if (wave_id() == kCtrlWave) {
-    const int lane = lane_id();
-    uint32_t ok = 1;
-    if (lane == 0) {
-      ok = poll_deps(a, t, indeg);
-      sm.flag = ok;
-      sm.t_ready = clock100();
-    }
-    ok = __builtin_amdgcn_readfirstlane(ok);
-    if (ok) {
-      const int K4 = K >> 2;
-      for (int b = 0; b < nb; ++b)
-        for (int c = 0; c < K4; c += 64)
-          if (c + lane < K4)
-            __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL f32x4*)x + (size_t)b * K4 + c + lane),
-                                             (__attribute__((address_space(3))) void*)(sm.xs + (size_t)b * K + 4 * c),
-                                             16, 0, kCachePolicySC1);
-      // gamma (weight dtype) in raw form: 8 bytes per 4 values in bf16, 16 in fp32.
-      typedef typename std::conditional<GBF16, u32x2, u32x4>::type graw_t;
-      constexpr int GB = 16;
-      for (int b = 0; b < nb; ++b) {
-        f32x4* xo = (f32x4*)(sm.xs + (size_t)b * K);
-        float ss = 0.f;
-        for (int c0 = 0; c0 < K4; c0 += 64 * GB) {
-          graw_t gv[GB];
-          if (norm) {
+                                                float rs[BM], bool spread) {
+  const bool ctrl = wave_id() == kCtrlWave;
+  const int lane = lane_id();
+  uint32_t ok = 1;
+  if (ctrl && lane == 0) {
+    ok = poll_deps(a, t, indeg);
+    sm.flag = ok;
+    sm.t_ready = clock100();
+  }
+  // spread (no norm, no LDS rows in this tile): no wave has a bulk prefetch queued
+  // ahead of its loads, so once the control wave has seen the producers every wave
+  // copies its share of the input (one wave's copies alone take a round trip per
+  // ~20 KB).  Both cases share one copy loop: a second copy site made the compiler's
+  // wait counts in the streaming loops drain the ring at every row.
+  if (spread) {
+    __syncthreads();
+    ok = sm.flag;
+  }
+  ok = __builtin_amdgcn_readfirstlane(ok);
+  if ((ctrl || spread) && ok) {
+    const int K4 = K >> 2;
+    const int cf = spread ? wave_id() * 64 : 0, cs = spread ? kThreads : 64;
+    for (int b = 0; b < nb; ++b)
+      for (int c = cf; c < K4; c += cs)
+        if (c + lane < K4)
+          __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL f32x4*)x + (size_t)b * K4 + c + lane),
+                                           (__attribute__((address_space(3))) void*)(sm.xs + (size_t)b * K + 4 * c),
+                                           16, 0, kCachePolicySC1);
+    // gamma (weight dtype) in raw form: 8 bytes per 4 values in bf16, 16 in fp32.
+    typedef typename std::conditional<GBF16, u32x2, u32x4>::type graw_t;
+    constexpr int GB = 16;
+    for (int b = 0; b < nb; ++b) {
+      f32x4* xo = (f32x4*)(sm.xs + (size_t)b * K);
+      float ss = 0.f;
+      for (int c0 = 0; c0 < K4; c0 += 64 * GB) {
+        graw_t gv[GB];
+        if (norm) {
 #pragma unroll
-            for (int u = 0; u < GB; ++u) {
-              const int k4 = c0 + u * 64 + lane;
-              gv[u] = ldg<graw_t>(gamma, k4 < K4 ? k4 : 0);
-            }
+          for (int u = 0; u < GB; ++u) {
+            const int k4 = c0 + u * 64 + lane;
+            gv[u] = ldg<graw_t>(gamma, k4 < K4 ? k4 : 0);
           }
-          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row's LDS copy has landed
-          if (norm) {
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row's LDS copy has landed
+        if (norm) {
 #pragma unroll
-            for (int u = 0; u < GB; ++u) {
-              const int k4 = c0 + u * 64 + lane;
-              if (k4 < K4) {
-                f32x4 v = xo[k4];
-                ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-                f32x4 gf;
-                if constexpr (GBF16) gf = f32x4{bf16_lo(gv[u].x), bf16_hi(gv[u].x), bf16_lo(gv[u].y), bf16_hi(gv[u].y)};
-                else gf = f32x4{__uint_as_float(gv[u].x), __uint_as_float(gv[u].y), __uint_as_float(gv[u].z),
-                                __uint_as_float(gv[u].w)};
-                xo[k4] = v * gf;
-              }
+          for (int u = 0; u < GB; ++u) {
+            const int k4 = c0 + u * 64 + lane;
+            if (k4 < K4) {
+              f32x4 v = xo[k4];
+              ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+              f32x4 gf;
+              if constexpr (GBF16) gf = f32x4{bf16_lo(gv[u].x), bf16_hi(gv[u].x), bf16_lo(gv[u].y), bf16_hi(gv[u].y)};
+              else gf = f32x4{__uint_as_float(gv[u].x), __uint_as_float(gv[u].y), __uint_as_float(gv[u].z),
+                              __uint_as_float(gv[u].w)};
+              xo[k4] = v * gf;
             }
           }
         }
-        if (norm) ss = wave_sum(ss);
-        if (lane == 0) sm.red[b] = norm ? 1.0f / sqrtf(ss / (float)K + eps) : 1.f;
       }
+      if (norm) ss = wave_sum(ss);
+      if (ctrl && lane == 0) sm.red[b] = norm ? 1.0f / sqrtf(ss / (float)K + eps) : 1.f;
     }
     // Trace mode: when the input was staged (mark 2; marks 0 and 1 are thread 0's).
-    if (a.trace != nullptr && lane == 0) sm.t_mark[2] = clock100();
+    if (a.trace != nullptr && ctrl && lane == 0) sm.t_mark[2] = clock100();
   }
   __syncthreads();
   // Every wave now waits for its own ring and LDS prefetch.  Written as the builtin
@@ -248,6 +257,7 @@ struct GemvPf {
   int PF;
   int xfl;
   char* pfw;
+  int cap;  // whole rows that fit one wave's share (the same for every wave; 0: none)
 };
 
 template <int KBR>
@@ -257,6 +267,7 @@ __device__ __forceinline__ GemvPf gemv_pf_plan(const GemvGeom& g, int B, int bp,
     p.xfl = (B * g.K + 3) & ~3;
     const int per_wave = ((kSmemBytes - 4 * p.xfl) / kWaves) & ~1023;
     const int pf = per_wave / (KBR * 1024);
+    p.cap = pf;
     p.PF = pf < g.NQ ? pf : g.NQ;
     p.pfw = (char*)(sm.xs + p.xfl) + g.wave * per_wave;
   }
@@ -350,7 +361,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     // for): staging code duplicated on two paths into the streaming loop made the
     // compiler's wait counts there drain the whole ring at every row.
     if (!gemv_wait_stage<BM, BF16>(a, t, b0 == 0 ? d.remaining_deps : 0, x + (size_t)b0 * g.K, aux, norm, g.K, nb,
-                                   a.rms_eps, sm, rs))
+                                   a.rms_eps, sm, rs, !norm && pf.cap == 0))
       return;
     if (b0 == 0) trace_mark(a, sm, 0);
     float park[BM];
