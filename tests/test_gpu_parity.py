@@ -372,6 +372,57 @@ def test_1b_greedy_4_steps():
     _big_parity("1b_b1", steps=4)
 
 
+def test_1b_schedulers_and_graph_replay_equal_persistent_bitwise():
+    w = workloads.get("1b_b1")
+    _say("1b_b1: level-synchronous, per-op and HIP-graph replay vs persistent, bitwise")
+    run = MkRun(w)
+    ref = run.step("persistent")
+    run.graph.mk_set_schedule(mk.MK_SCHED_LEVELS)
+    assert np.array_equal(run.step("persistent"), ref), "levels"
+    run.graph.mk_set_schedule(mk.MK_SCHED_STATIC)
+    assert np.array_equal(run.step("per_op"), ref), "per-op"
+    run.graph.mk_capture_per_op_graph(*run.inp.step_ptrs())
+    run.inp.logits.zero_()
+    run.graph.mk_launch_per_op_graph(run.stream)
+    assert run.graph.mk_status() == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(run.inp.logits.cpu().numpy().astype(np.float64), ref), "graph replay"
+    assert np.array_equal(run.step("persistent"), ref), "persistent again"
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
+def test_1b_device_greedy_loop_equals_host_loop():
+    # The host loop (decode step, argmax of the copied logits, next position) is the
+    # path the 4-step oracle test above checks; the device loop must give its tokens.
+    n = 4
+    w = workloads.get("1b_b1").with_steps(n)
+    _say("1b_b1: 4 greedy steps, device loop (mk_decode_greedy) vs host loop")
+    run = MkRun(w)
+    tok0, pos0 = w.tokens(), workloads.get("1b_b1").positions()
+    tok, pos, host = tok0, pos0, []
+    for _ in range(n):
+        run.inp.set_step(tok, pos)
+        logits = run.step("persistent")
+        tok = np.array([od.greedy_token(logits[0])], dtype=np.int32)
+        host.append(int(tok[0]))
+        pos = pos + 1
+    last = logits
+    run.inp.refill_caches()
+    run.inp.set_step(tok0, pos0)
+    out = torch.full((n * w.batch,), -1, dtype=torch.int32, device="cuda")
+    run.graph.mk_decode_greedy(run.stream, n, *run.inp.step_ptrs(), out.data_ptr())
+    assert run.graph.mk_status() == 0
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == host
+    assert np.array_equal(run.inp.logits.cpu().numpy().astype(np.float64), last)
+    assert run.inp.positions.cpu().tolist() == pos.tolist()
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
 def test_8b_b1_step():
     _big_parity("8b_b1")
 
