@@ -511,10 +511,11 @@ int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t
 
 int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev, int32_t* positions_dev,
                      void* kcache_dev, void* vcache_dev, float* logits_dev, int32_t* tokens_out_dev) {
+  if (!g) return mk::set_error(MK_ERR_INVALID, "graph is NULL");
   if (n_steps < 0) return mk::set_error(MK_ERR_INVALID, "n_steps < 0");
   if (misaligned(tokens_out_dev, 4)) return mk::set_error(MK_ERR_ALIGN, "tokens_out must be 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  const int batch = g ? g->low.cfg.batch : 0;
+  const int batch = g->low.cfg.batch;
   for (int i = 0; i < n_steps; ++i) {
     int rc = mk_decode_step(g, stream, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
     if (rc) return rc;

@@ -109,3 +109,19 @@ def test_scratch_layout():
     assert spans[-1][0] + spans[-1][1] <= mk.mk_plan(cfg)["scratch_bytes"]
     with pytest.raises(mk.MkError):
         lo.scratch_span(bi.w_lm)
+
+
+def test_step_entry_points_reject_bad_arguments_without_a_gpu():
+    # Argument checks run before any HIP call, so they answer on a machine with no GPU.
+    L = binding.lib()
+    tok = ctypes.c_void_p(16)
+    err = [
+        L.mk_sample_greedy(None, None, tok, tok, tok),
+        L.mk_decode_greedy(None, None, 1, tok, tok, tok, tok, tok, None),
+        L.mk_capture_per_op_graph(None, tok, tok, tok, tok, tok),
+        L.mk_launch_per_op_graph(None, None),
+        L.mk_decode_step(None, None, tok, tok, tok, tok, tok),
+        L.mk_set_schedule(None, binding.MK_SCHED_LEVELS),
+    ]
+    assert err == [binding.MK_ERR_INVALID] * len(err)
+    assert "NULL" in mk.mk_last_error()
