@@ -317,6 +317,27 @@ def main():
     achieved = bytes_step / (ms / 1e3) / 1e9
     log(f"persistent: {ms:.4f} ms/step, {tok_s:.1f} tok/s, {achieved:.0f} GB/s")
 
+    # Secondary denominator: what a plain streaming read reaches on this part (2 GiB,
+    # well past the 256 MB memory-side cache), timed the same way on the same stream.
+    from synth import native
+    n_read = 2 << 30
+    src = torch.empty(n_read, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        native.gpu_read(src.data_ptr(), n_read, sink.data_ptr(), 2048, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        native.gpu_read(src.data_ptr(), n_read, sink.data_ptr(), 2048, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 5 * n_read / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, sink
+    stream_ceiling = {"value": stream_gbs, "unit": "GB/s", "bytes": n_read, "kernel": "read16_kernel (plain read)",
+                      "frac": achieved / stream_gbs}
+    log(f"streaming-read ceiling: {stream_gbs:.0f} GB/s; the step reaches {achieved / stream_gbs:.3f} of it")
+
     alt = None
     if not args.no_alt_schedule:
         # The other schedule modes on the same graph: dynamic tickets, and the
@@ -413,6 +434,7 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "per_op_baseline": per_op,
         "other_schedule": alt,
+        "stream_ceiling": stream_ceiling,
         "greedy": greedy,
         "cpu_baseline": cpu,
     }

@@ -98,3 +98,44 @@ extern "C" int synth_gpu_copy(void* dst, const void* src, uint64_t n_bytes, void
                        (uint4*)dst, n_bytes / 16);
     return (int)hipGetLastError();
 }
+
+// A plain streaming read of n 16-byte words: every byte read once, one word per
+// workgroup written (the XOR of what it read, so the loads are kept).  The measured
+// ceiling of a read-only stream on this part, beside the published peak.  Eight
+// independent 16-byte non-temporal loads per thread and iteration (the weight streams'
+// access kind) keep enough bytes in flight.
+typedef unsigned int read_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read16_kernel(const read_u32x4* __restrict__ src, uint64_t n, uint32_t* out) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; j + 7 * stride < n; j += 8 * stride) {
+        read_u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + j + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; j < n; j += stride) {
+        const read_u32x4 a = __builtin_nontemporal_load(src + j);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int i = 0; i < 256; ++i) r ^= red[i];
+        out[blockIdx.x] = r;
+    }
+}
+
+// out: blocks uint32 words (device).  n_bytes a multiple of 16.
+extern "C" int synth_gpu_read(const void* src, uint64_t n_bytes, void* out, uint32_t blocks, void* stream) {
+    if (n_bytes % 16 != 0 || blocks == 0) return (int)hipErrorInvalidValue;
+    if (n_bytes == 0) return 0;
+    hipLaunchKernelGGL(read16_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const read_u32x4*)src,
+                       n_bytes / 16, (uint32_t*)out);
+    return (int)hipGetLastError();
+}

@@ -66,6 +66,8 @@ def gpu_lib():
         lib.synth_gpu_fill_cache.argtypes = [vp, ctypes.c_int, u64, u64, u64, u64, u64, u64, dbl, dbl, vp]
         lib.synth_gpu_copy.argtypes = [vp, vp, u64, vp]
         lib.synth_gpu_copy.restype = ctypes.c_int
+        lib.synth_gpu_read.argtypes = [vp, u64, vp, ctypes.c_uint32, vp]
+        lib.synth_gpu_read.restype = ctypes.c_int
         lib.synth_gpu_fill_cache.restype = ctypes.c_int
         _gpu = lib
     return _gpu
@@ -120,3 +122,10 @@ def gpu_copy(dst_ptr: int, src_ptr: int, n_bytes: int, stream: int = 0) -> None:
     rc = gpu_lib().synth_gpu_copy(dst_ptr, src_ptr, n_bytes, stream)
     if rc != 0:
         raise RuntimeError(f"synth_gpu_copy failed ({rc})")
+
+
+def gpu_read(src_ptr: int, n_bytes: int, out_ptr: int, blocks: int, stream: int = 0) -> None:
+    """Plain streaming read of n_bytes (a multiple of 16); out_ptr: `blocks` uint32 words."""
+    rc = gpu_lib().synth_gpu_read(src_ptr, n_bytes, out_ptr, blocks, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_gpu_read failed ({rc})")
