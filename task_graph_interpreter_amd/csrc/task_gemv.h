@@ -112,6 +112,41 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
   }
 }
 
+// Two weight rows against one staged input row (batch 1): the input chunk is read
+// from LDS once for both rows (the LDS-resident rows are bound by LDS reads, and the
+// input is twice the bytes of a bf16 weight chunk).
+template <bool BF16>
+__device__ __forceinline__ void gemv_consume_pair(const u32x4 w0, const u32x4 w1, const float* xs, int chunk,
+                                                  bool valid, float& a0, float& a1) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  float f0[8], f1[8];
+  if (BF16) {
+    f0[0] = bf16_lo(w0.x); f0[1] = bf16_hi(w0.x); f0[2] = bf16_lo(w0.y); f0[3] = bf16_hi(w0.y);
+    f0[4] = bf16_lo(w0.z); f0[5] = bf16_hi(w0.z); f0[6] = bf16_lo(w0.w); f0[7] = bf16_hi(w0.w);
+    f1[0] = bf16_lo(w1.x); f1[1] = bf16_hi(w1.x); f1[2] = bf16_lo(w1.y); f1[3] = bf16_hi(w1.y);
+    f1[4] = bf16_lo(w1.z); f1[5] = bf16_hi(w1.z); f1[6] = bf16_lo(w1.w); f1[7] = bf16_hi(w1.w);
+  } else {
+    f0[0] = __uint_as_float(w0.x); f0[1] = __uint_as_float(w0.y); f0[2] = __uint_as_float(w0.z);
+    f0[3] = __uint_as_float(w0.w);
+    f1[0] = __uint_as_float(w1.x); f1[1] = __uint_as_float(w1.y); f1[2] = __uint_as_float(w1.z);
+    f1[3] = __uint_as_float(w1.w);
+    f0[4] = f0[5] = f0[6] = f0[7] = f1[4] = f1[5] = f1[6] = f1[7] = 0.f;
+  }
+  const float m = valid ? 1.f : 0.f;  // a masked chunk contributes 0
+  const f32x4* xb = (const f32x4*)(xs + (valid ? chunk : 0) * VEC);
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC / 4; ++e) {
+    const f32x4 xv = xb[e];
+    s0 = fmaf(f0[4 * e + 0], xv.x, s0); s1 = fmaf(f1[4 * e + 0], xv.x, s1);
+    s0 = fmaf(f0[4 * e + 1], xv.y, s0); s1 = fmaf(f1[4 * e + 1], xv.y, s1);
+    s0 = fmaf(f0[4 * e + 2], xv.z, s0); s1 = fmaf(f1[4 * e + 2], xv.z, s1);
+    s0 = fmaf(f0[4 * e + 3], xv.w, s0); s1 = fmaf(f1[4 * e + 3], xv.w, s1);
+  }
+  a0 = fmaf(s0, m, a0);
+  a1 = fmaf(s1, m, a1);
+}
+
 // Wait for the tile's producers and stage its input rows 0 .. nb-1 (x * gamma with
 // RMS_NORM_INPUT) into LDS, both on the control wave alone (spread: the copies are
 // shared by every wave, see below), then meet the other waves at one barrier; returns r_b (1 without the norm) in rs[], or false if the step was
@@ -424,7 +459,24 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     }
     if (g.NQ > 0) {
       if (KBT > 0) {
-        for (int q = 0; q < PF; ++q) {
+        int q = 0;
+        if constexpr (BM == 1 && KBR <= 8) {
+          for (; q + 1 < PF; q += 2) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll 2
+            for (int kb = 0; kb < KBR; ++kb) {
+              const u32x4 w0 = *(const u32x4*)(pfw + (q * KBR + kb) * 1024 + 16 * lane);
+              const u32x4 w1 = *(const u32x4*)(pfw + ((q + 1) * KBR + kb) * 1024 + 16 * lane);
+              const int chunk = kb * 64 + lane;
+              gemv_consume_pair<BF16>(w0, w1, sm.xs, chunk, chunk < g.KC, a0, a1);
+            }
+            const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(a0)), 63));
+            const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(a1)), 63));
+            park[0] = (lane == (q & 63)) ? v0 * rs[0] : park[0];
+            park[0] = (lane == ((q + 1) & 63)) ? v1 * rs[0] : park[0];
+          }
+        }
+        for (; q < PF; ++q) {
           float acc[BM];
 #pragma unroll
           for (int b = 0; b < BM; ++b) acc[b] = 0.f;
