@@ -202,8 +202,9 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
  * index holding the largest value of logits_dev row b ([batch, vocab] fp32; NaN never
  * wins, a row with no comparable value gives 0), and positions_dev[b] += 1, ready
  * for the next step.  One workgroup per row; batch and vocab are the graph's.  Runs as
- * its own small kernel after the step rather than as tasks of the graph.  Errors:
- * MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP. */
+ * its own small kernel after the step rather than as tasks of the graph.  While the
+ * graph's device status word holds a failure (see mk_status) it writes nothing: tokens
+ * and positions keep their values.  Errors: MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP. */
 int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t* tokens_dev,
                      int32_t* positions_dev);
 
@@ -213,7 +214,8 @@ int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t
  * (device, n_steps * batch int32), step i's tokens are also written to
  * tokens_out_dev[i * batch + b].  Positions must stay below each sequence's kv_len
  * (the graph's chunk fan-out); a step past it sets MK_STATUS_BAD_POSITION, which
- * mk_status reports.  Same errors as mk_decode_step. */
+ * mk_status reports.  From a failed step on, the later steps run no task and their
+ * SAMPLE writes no token and advances no position.  Same errors as mk_decode_step. */
 int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev, int32_t* positions_dev,
                      void* kcache_dev, void* vcache_dev, float* logits_dev, int32_t* tokens_out_dev);
 

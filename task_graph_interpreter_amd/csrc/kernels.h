@@ -245,6 +245,12 @@ template <class S>
 __global__ __launch_bounds__(kThreads, 1) void level_kernel(LaunchArgs a) {
   __shared__ Smem sm;
   const uint32_t G = gridDim.x;
+  // A step after a failed one (sticky status word, cleared by mk_status) runs
+  // nothing; a workgroup that leaves here never arrives at a barrier, and the
+  // others' barrier polls give up on the same status word.
+  if (threadIdx.x == 0) sm.flag = read_status(a) == 0;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sm.flag) == 0) return;
   for (uint32_t lv = 0; lv < a.n_levels; ++lv) {
     const uint32_t b = ldg<uint32_t>(a.lvl_off, lv), e = ldg<uint32_t>(a.lvl_off, lv + 1);
     for (uint32_t i = b + blockIdx.x; i < e; i += G) {

@@ -63,10 +63,12 @@ static const SpecEntry* select_spec(const mk_model_cfg& c) {
 // vocabulary), one workgroup per batch row: tokens[b] = the lowest index holding the
 // row's largest logit (NaN never wins; a row with no comparable value gives 0), also
 // written to out[b] when out is non-null, and positions[b] += 1 for the next step.
+// After a failed step (non-zero status word) the logits are not trusted: tokens,
+// out and positions are left as they are.
 constexpr int kSampleThreads = 256;
 __global__ __launch_bounds__(kSampleThreads) void sample_greedy_kernel(const float* logits, int vocab,
                                                                         int32_t* tokens, int32_t* positions,
-                                                                        int32_t* out) {
+                                                                        int32_t* out, const Ctrl* ctrl) {
   const int b = blockIdx.x;
   const float* row = logits + (size_t)b * vocab;
   float best = -INFINITY;
@@ -94,6 +96,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_greedy_kernel(const flo
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    const uint32_t status =
+        __hip_atomic_load((const MK_GLOBAL uint32_t*)&ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (status != 0) return;
     for (int w = 1; w < kSampleThreads / 64; ++w)
       if (sb[w] > best || (sb[w] == best && si[w] < bi)) {
         best = sb[w];
@@ -503,7 +508,7 @@ int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t
   hipStream_t s = (hipStream_t)stream;
   const mk_model_cfg& c = g->low.cfg;
   hipLaunchKernelGGL(mk::sample_greedy_kernel, dim3(c.batch), dim3(mk::kSampleThreads), 0, s, logits_dev, c.vocab,
-                     tokens_dev, positions_dev, (int32_t*)nullptr);
+                     tokens_dev, positions_dev, (int32_t*)nullptr, g->d_ctrl);
   HIP_TRY(hipGetLastError());
   g->last_stream = s;
   return MK_OK;
@@ -521,7 +526,7 @@ int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev
     if (rc) return rc;
     hipLaunchKernelGGL(mk::sample_greedy_kernel, dim3(batch), dim3(mk::kSampleThreads), 0, s, logits_dev,
                        g->low.cfg.vocab, tokens_dev, positions_dev,
-                       tokens_out_dev ? tokens_out_dev + (size_t)i * batch : (int32_t*)nullptr);
+                       tokens_out_dev ? tokens_out_dev + (size_t)i * batch : (int32_t*)nullptr, g->d_ctrl);
     HIP_TRY(hipGetLastError());
   }
   return MK_OK;

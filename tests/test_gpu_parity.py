@@ -2,8 +2,10 @@
 
 Every test builds a graph with mk_build_graph, runs mk_decode_step (the persistent
 interpreter) and/or mk_decode_step_per_op (one launch per op, same task bodies) and
-compares logits within |gpu - ref| <= 2e-2 + 1e-2 |ref|, greedy tokens exactly, and
-(on the small workloads) every activation buffer of the step.
+compares logits within |gpu - ref| <= 2e-2 + 1e-2 |ref| and within the tighter bound of
+the arithmetic path (gpu_common.TIERS), greedy tokens exactly (a row is exempt only
+when the oracle's own top-2 margin is below what that bound lets two logits move),
+and (on the small workloads) every activation buffer of the step.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ from oracle.params import GeneratedParams
 from synth import gen, native, workloads
 from synth.device import DeviceInputs
 
-from gpu_common import MkRun, check_close, check_tokens, compare_activations
+from gpu_common import TIERS, MkRun, check_close, check_logits, check_tokens, compare_activations, tier_of
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +37,17 @@ def _device():
 def _oracle(w, keep=False, rows=None, split=False):
     p = GeneratedParams(w)
     return od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), rows=rows, keep=keep, split=split)
+
+
+def _check_step(w, logits, ref, what="logits"):
+    """Logits at the contract and the path's tier, then exact greedy tokens; returns
+    (max |dlogit|, GPU tokens, oracle tokens)."""
+    err = check_logits(logits, ref, w, what)
+    toks, exempt = check_tokens(logits, ref, TIERS[tier_of(w)], what)
+    ref_toks = [od.greedy_token(r) for r in ref]
+    _say(f"{what}: max|dlogit|={err:.2e} tokens={toks} oracle={ref_toks} exempt rows={exempt} "
+         f"min oracle top-2 margin={min(od.top2_margin(r) for r in ref):.2e}")
+    return err, toks, ref_toks
 
 
 def test_fill_kernel_matches_generator():
@@ -59,8 +72,7 @@ def test_tiny_step_all_activations(path):
     logits = run.step(path)
     ref, inter = _oracle(w, keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
-    check_close(logits, ref, "logits")
-    assert od.greedy_token(logits[0]) == od.greedy_token(ref[0])
+    _check_step(w, logits, ref)
     run.close()
 
 
@@ -122,8 +134,7 @@ def test_tiny_variants_bf16_batch_ragged(joins, mode):
     logits = run.step("persistent")
     ref, inter = _oracle(w, keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
-    check_close(logits, ref, "logits")
-    assert [od.greedy_token(r) for r in logits] == [od.greedy_token(r) for r in ref]
+    _check_step(w, logits, ref)
     run.close()
 
 
@@ -154,8 +165,7 @@ def test_tiny_mfma_gemv_all_activations(case):
     logits = run.step("persistent")
     ref, inter = _oracle(w, keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
-    check_close(logits, ref, "logits")
-    check_tokens(logits, ref)
+    _check_step(w, logits, ref)
     again = run.step("per_op")
     assert np.array_equal(logits, again), "per-op and persistent MFMA paths differ"
     run.close()
@@ -173,8 +183,7 @@ def test_8b_shapes_2_layers_b32_mfma_all_activations():
     p = GeneratedParams(w, backend="c")
     ref, inter = od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
-    check_close(logits, ref, "logits")
-    check_tokens(logits, ref)
+    _check_step(w, logits, ref)
     run.close()
     del run
     torch.cuda.empty_cache()
@@ -193,10 +202,8 @@ def test_tiny_greedy_8_steps(path):
         run.inp.set_step(tok, pos)
         logits = run.step(path)
         ref, _ = od.decode_step(w, p, tok, pos, kv)
-        check_close(logits, ref, f"logits step {s}")
-        t_gpu, t_ref = od.greedy_token(logits[0]), od.greedy_token(ref[0])
-        assert t_gpu == t_ref, (s, t_gpu, t_ref, od.top2_margin(ref[0]))
-        tok = np.array([t_ref], dtype=np.int32)
+        _, _, t_ref = _check_step(w, logits, ref, f"logits step {s}")
+        tok = np.array(t_ref, dtype=np.int32)
         pos = pos + 1
     run.close()
 
@@ -243,7 +250,7 @@ def test_device_greedy_loop_8_steps():
         assert got[s, 0] == t_ref, (s, int(got[s, 0]), t_ref, od.top2_margin(ref[0]))
         tok = np.array([t_ref], dtype=np.int32)
         pos = pos + 1
-    check_close(run.inp.logits.cpu().numpy().astype(np.float64), ref, "logits of the last step")
+    check_logits(run.inp.logits.cpu().numpy().astype(np.float64), ref, w, "logits of the last step")
     assert run.inp.tokens.cpu().tolist() == [int(got[7, 0])]
     assert run.inp.positions.cpu().tolist() == pos.tolist()
     run.close()
@@ -262,6 +269,46 @@ def test_bad_position_reports_status_then_recovers():
     run.inp.refill_caches()
     again = run.step("persistent")
     assert np.array_equal(good, again)
+    run.close()
+
+
+@pytest.mark.parametrize("mode", ["static", "levels"])
+def test_step_after_a_failed_step_runs_nothing(mode):
+    # A step enqueued while the status word still holds an earlier failure (no
+    # mk_status in between) runs no task: its logits stay as they were.
+    w = workloads.tiny()
+    _say(f"tiny step after a failed step, {mode} lists")
+    run = MkRun(w)
+    run.graph.mk_set_schedule(SCHED[mode])
+    good = run.step("persistent")
+    run.inp.set_step(w.tokens(), np.array([w.kv_capacity], dtype=np.int32))
+    run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
+    run.inp.set_step(w.tokens(), w.positions())
+    run.inp.refill_caches()
+    run.inp.logits.fill_(7.0)
+    run.graph.mk_decode_step(run.stream, *run.inp.step_ptrs())
+    torch.cuda.synchronize()
+    assert (run.inp.logits == 7.0).all()
+    assert run.graph.mk_status() & 0xF0000000 == 0x20000000
+    assert np.array_equal(run.step("persistent"), good)
+    run.close()
+
+
+def test_greedy_loop_after_a_failed_step_writes_no_token():
+    # mk_decode_greedy from an out-of-range position: the first step fails, its SAMPLE
+    # and every later step and SAMPLE leave tokens, positions and tokens_out alone.
+    w = workloads.tiny().with_steps(4)
+    _say("tiny greedy loop from a bad position")
+    run = MkRun(w)
+    bad = np.array([w.kv_capacity], dtype=np.int32)
+    run.inp.set_step(w.tokens(), bad)
+    out = torch.full((3 * w.batch,), -1, dtype=torch.int32, device="cuda")
+    run.graph.mk_decode_greedy(run.stream, 3, *run.inp.step_ptrs(), out.data_ptr())
+    st = run.graph.mk_status()
+    assert st & 0xF0000000 == 0x20000000
+    assert out.cpu().tolist() == [-1, -1, -1]
+    assert run.inp.positions.cpu().tolist() == bad.tolist()
+    assert run.inp.tokens.cpu().tolist() == w.tokens().tolist()
     run.close()
 
 
@@ -342,6 +389,10 @@ def test_trace_mode_records_every_task(mode):
 
 
 def _big_parity(name, rows=None, steps=1):
+    """``steps`` greedy steps of a full-size workload on the persistent kernel against
+    the oracle (all batch rows, or the sampled ``rows``: rows are independent, so the
+    oracle computes exactly those).  Both sides take the oracle's tokens as the next
+    step's input, after the GPU's tokens were asserted equal to them."""
     w = workloads.get(name)
     if steps > 1:
         w = w.with_steps(steps)
@@ -356,12 +407,10 @@ def _big_parity(name, rows=None, steps=1):
         run.inp.set_step(tok, pos)
         logits = run.step("persistent")
         ref, _ = od.decode_step(w, p, tok, pos, kv, rows=rows)
-        err = check_close(logits[rows], ref, f"{name} logits step {s}")
-        t_ref = [od.greedy_token(r) for r in ref]
-        ties = check_tokens(logits[rows], ref, f"{name} step {s}")
-        _say(f"{name} step {s}: max|dlogit|={err:.2e} tokens={t_ref} ties within error={ties} "
-             f"min top-2 margin={min(od.top2_margin(r) for r in ref):.2e}")
-        tok = np.array([od.greedy_token(logits[b]) for b in range(w.batch)], dtype=np.int32)
+        _, _, t_ref = _check_step(w, logits[rows], ref, f"{name} step {s}")
+        if steps > 1:
+            assert rows == list(range(w.batch))
+            tok = np.array(t_ref, dtype=np.int32)
         pos = pos + 1
     run.close()
     del run

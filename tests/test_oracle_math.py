@@ -96,6 +96,48 @@ def test_split_and_combine_equal_unsplit(chunk):
     np.testing.assert_allclose(od.combine(parts), od.softmax_attention(q, K, V), rtol=1e-12, atol=1e-13)
 
 
+def test_chunk_partial_m_and_l_brute_force():
+    # m is the largest score and l the sum of e^(s - m), each from explicit loops
+    # over keys and dimensions; o against the same loop.  A wrong m with a matching
+    # l would cancel in the merge, so they are pinned here on their own.
+    n, hd = 23, 8
+    q = RNG.standard_normal(hd) * 2
+    K, V = RNG.standard_normal((n, hd)), RNG.standard_normal((n, hd))
+    scores = []
+    for j in range(n):
+        acc = 0.0
+        for d in range(hd):
+            acc += q[d] * K[j, d]
+        scores.append(acc / np.sqrt(hd))
+    mx = scores[0]
+    for s in scores[1:]:
+        mx = s if s > mx else mx
+    l_ref, o_ref = 0.0, np.zeros(hd)
+    for j in range(n):
+        e = np.exp(scores[j] - mx)
+        l_ref += e
+        o_ref = o_ref + e * V[j]
+    m, l, o = od.chunk_partial(q, K, V)
+    assert m == pytest.approx(mx, rel=1e-14, abs=1e-14)
+    assert l == pytest.approx(l_ref, rel=1e-13)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    # the largest term of l is e^0 = 1, so 1 <= l <= n
+    assert 1.0 <= l <= n
+
+
+def test_chunk_partial_single_key():
+    q, k, v = RNG.standard_normal(4), RNG.standard_normal((1, 4)), RNG.standard_normal((1, 4))
+    m, l, o = od.chunk_partial(q, k, v)
+    assert m == pytest.approx(float(q @ k[0]) / 2.0, rel=1e-14)  # sqrt(4) = 2
+    assert l == 1.0
+    np.testing.assert_array_equal(o, v[0])
+
+
+def test_top2_margin():
+    assert od.top2_margin(np.array([1.0, 5.0, 3.0])) == 2.0
+    assert od.top2_margin(np.array([4.0, -1.0, 4.0])) == 0.0
+
+
 def test_empty_chunk_partial():
     m, l, o = od.chunk_partial(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)))
     assert m == -np.inf and l == 0.0 and (o == 0).all()
