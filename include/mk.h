@@ -171,9 +171,14 @@ int mk_lowered_levels(mk_lowered* g, const uint32_t** tasks, const uint32_t** of
 void mk_lowered_free(mk_lowered* g);
 
 /* Lower, then upload descriptors + edges (one blob behind a 64-byte header) and the
- * buffer table to the device, on `stream`.  `scratch_dev` (device pointer, at least
- * mk_plan().scratch_bytes, 256-byte aligned) holds the step's activations.  The
- * weights must stay valid for the graph's lifetime. */
+ * buffer table to the device, on `stream` ("Mega kernel initial": the lowering, edge
+ * and upload sections; the buffer table holds indices, the pointers live in a table
+ * of their own).  `scratch_dev` (device pointer, at least mk_plan().scratch_bytes,
+ * 256-byte aligned) holds the step's activations; NULL builds a graph that only
+ * mk_decode_step_noalloc can run.  The weights must stay valid for the graph's
+ * lifetime.  Synchronises `stream` before returning.  Errors: MK_ERR_ABI,
+ * MK_ERR_INVALID (configuration or weights), MK_ERR_ALIGN, MK_ERR_NOMEM, MK_ERR_HIP;
+ * *out is NULL on failure. */
 int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scratch_dev,
                    void* stream, mk_graph** out);
 
@@ -190,6 +195,25 @@ int mk_graph_edges(const mk_graph* g, const uint32_t** edges, uint32_t* n);
  * (mk_status) and leave the outputs of the affected sequence undefined. */
 int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
                    void* kcache_dev, void* vcache_dev, float* logits_dev);
+
+/* For callers that cannot allocate device memory at step time (code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid allocation): mk_decode_step with
+ * the step's activations in a static array of the library instead of the caller's
+ * scratch block.  Same kernels, same descriptors, same arguments and results as
+ * mk_decode_step.  It calls no hipMalloc, hipFree or other allocating routine.
+ *   - The array is a file-scope device array of 64 MiB (MK_STATIC_SCRATCH_BYTES); each
+ *     device the library runs on holds its own copy until the process ends.  A graph
+ *     whose mk_plan scratch_bytes exceed it is rejected with MK_ERR_INVALID.
+ *   - Its address on a device is taken once, when a graph is built on that device.
+ *   - Every call on one device shares that device's array: calls that overlap on one
+ *     device (several streams, or several graphs, without stream order between them)
+ *     race and give undefined results.  Each step writes every activation it reads,
+ *     so nothing has to be cleared between calls.
+ *   - A graph built with scratch_dev = NULL can run only through this call.
+ * Errors: as mk_decode_step, plus MK_ERR_INVALID for a graph beyond the limit. */
+#define MK_STATIC_SCRATCH_BYTES (64ull << 20)
+int mk_decode_step_noalloc(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
+                           void* kcache_dev, void* vcache_dev, float* logits_dev);
 
 /* The same step with the same task bodies and descriptors, one kernel launch per op
  * (stream order instead of readiness counters): the per-op-launch baseline. */

@@ -21,6 +21,7 @@ MK_OK, MK_ERR_ABI, MK_ERR_INVALID, MK_ERR_ALIGN, MK_ERR_HIP, MK_ERR_NOMEM, MK_ER
 MK_STATUS_TIMEOUT, MK_STATUS_BAD_POSITION, MK_STATUS_BAD_TOKEN = 0x10000000, 0x20000000, 0x30000000
 MK_STATUS_KIND_MASK = 0xF0000000
 MK_SCHED_STATIC, MK_SCHED_DYNAMIC, MK_SCHED_LEVELS = 0, 1, 2
+MK_STATIC_SCRATCH_BYTES = 64 << 20
 # OpIds and flag bits of the descriptor (mk.h).
 (MK_OP_NOP, MK_OP_MEMCPY, MK_OP_GEMV, MK_OP_RMSNORM, MK_OP_ATTENTION, MK_OP_MLP, MK_OP_SAMPLE,
  MK_OP_ATTENTION_APPEND, MK_OP_ATTENTION_PARTIAL, MK_OP_ATTENTION_COMBINE) = range(10)
@@ -39,7 +40,7 @@ MK_DTYPE = {"f32": 0, "bf16": 1}
 # Every symbol include/mk.h declares.
 EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
            "mk_lowered_levels", "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
-           "mk_decode_step_per_op", "mk_sample_greedy", "mk_decode_greedy", "mk_capture_per_op_graph",
+           "mk_decode_step_noalloc", "mk_decode_step_per_op", "mk_sample_greedy", "mk_decode_greedy", "mk_capture_per_op_graph",
            "mk_launch_per_op_graph", "mk_status",
            "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid", "mk_graph_kernel_name", "mk_set_schedule", "mk_graph_schedule", "mk_lowered_schedule", "mk_destroy", "mk_last_error", "mk_abi_version"]
 
@@ -103,6 +104,7 @@ def lib():
         "mk_graph_tasks": ([vp, P(P(MkTask)), P(u32)], i32),
         "mk_graph_edges": ([vp, P(P(u32)), P(u32)], i32),
         "mk_decode_step": ([vp, vp, vp, vp, vp, vp, vp], i32),
+        "mk_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "mk_decode_step_per_op": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "mk_sample_greedy": ([vp, vp, vp, vp, vp], i32),
         "mk_decode_greedy": ([vp, vp, i32, vp, vp, vp, vp, vp, vp], i32),
@@ -240,6 +242,9 @@ class Graph:
 
     def mk_decode_step(self, stream, tokens, positions, kcache, vcache, logits) -> None:
         _check(lib().mk_decode_step(self.h, stream, tokens, positions, kcache, vcache, logits))
+
+    def mk_decode_step_noalloc(self, stream, tokens, positions, kcache, vcache, logits) -> None:
+        _check(lib().mk_decode_step_noalloc(self.h, stream, tokens, positions, kcache, vcache, logits))
 
     def mk_decode_step_per_op(self, stream, tokens, positions, kcache, vcache, logits) -> None:
         _check(lib().mk_decode_step_per_op(self.h, stream, tokens, positions, kcache, vcache, logits))

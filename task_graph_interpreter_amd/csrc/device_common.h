@@ -32,8 +32,11 @@ constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kCachePolicyNT = 2;
 
 // Buffer-table entry tags (top byte): 0 = absolute device pointer; otherwise an
-// offset into a per-step base passed at launch.
-enum : uint32_t { TAG_ABS = 0, TAG_KCACHE = 1, TAG_VCACHE = 2, TAG_TOKENS = 3, TAG_POSITIONS = 4, TAG_LOGITS = 5 };
+// offset into a base passed at launch: the per-step buffers, and the activation
+// scratch block (the caller's workspace, or the library's static array).
+enum : uint32_t {
+  TAG_ABS = 0, TAG_KCACHE = 1, TAG_VCACHE = 2, TAG_TOKENS = 3, TAG_POSITIONS = 4, TAG_LOGITS = 5, TAG_SCRATCH = 6
+};
 constexpr uint64_t kTagShift = 56;
 constexpr uint64_t kOffMask = (uint64_t(1) << kTagShift) - 1;
 
@@ -164,6 +167,7 @@ __device__ __forceinline__ char* resolve(const LaunchArgs& a, uint32_t idx) {
   base = tag == TAG_TOKENS ? a.rt[TAG_TOKENS] : base;
   base = tag == TAG_POSITIONS ? a.rt[TAG_POSITIONS] : base;
   base = tag == TAG_LOGITS ? a.rt[TAG_LOGITS] : base;
+  base = tag == TAG_SCRATCH ? a.rt[TAG_SCRATCH] : base;
   return (char*)(base + (e & kOffMask));
 }
 

@@ -90,6 +90,7 @@ struct Levels {
 void build_levels(const Lowered& L, Levels& out);
 
 int set_error(int code, const std::string& msg);
+int set_error(int code, const char* msg);  // allocates nothing
 
 }  // namespace mk
 

@@ -455,18 +455,22 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
   return MK_OK;
 }
 
-static thread_local std::string g_last_error;
+// The last error message of the calling thread, in a fixed buffer: recording an
+// error allocates nothing, so entry points that must not allocate can report one.
+static thread_local char g_last_error[512];
 
-int set_error(int code, const std::string& msg) {
-  g_last_error = msg;
+int set_error(int code, const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg ? msg : "");
   return code;
 }
+
+int set_error(int code, const std::string& msg) { return set_error(code, msg.c_str()); }
 
 }  // namespace mk
 
 extern "C" {
 
-const char* mk_last_error(void) { return mk::g_last_error.c_str(); }
+const char* mk_last_error(void) { return mk::g_last_error; }
 
 uint32_t mk_abi_version(void) { return MK_ABI_VERSION; }
 

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -111,6 +112,18 @@ __global__ __launch_bounds__(kSampleThreads) void sample_greedy_kernel(const flo
   }
 }
 
+// Activation scratch of mk_decode_step_noalloc, for callers that cannot allocate: a
+// file-scope device array, one copy per device, held until the process ends.  In host
+// code `scratch` is a host-side stand-in for the symbol, not a device address: the
+// address comes from hipGetSymbolAddress, taken once per device (with that device
+// current) when a graph is built there, and kept in scratch_dev[].
+constexpr uint64_t kStaticScratchBytes = uint64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
 __global__ void reset_kernel(uint32_t* arrivals, uint32_t n, Ctrl* ctrl) {
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
     arrivals[(size_t)i * kArrivalStride] = 0;
@@ -139,6 +152,7 @@ struct mk_graph {
   mk::Schedule sched;
   int sched_mode = MK_SCHED_STATIC;
   uint64_t* d_table = nullptr;
+  void* scratch = nullptr;           // caller's activation workspace (may be null: mk_decode_step_noalloc only)
   uint32_t* d_arrivals = nullptr;
   mk::Ctrl* d_ctrl = nullptr;
   uint64_t* d_trace = nullptr;
@@ -153,8 +167,12 @@ struct mk_graph {
 
 namespace {
 
+// Records "what: HIP's message" without allocating (entry points that must not
+// allocate report HIP failures through it too).
 int hip_fail(hipError_t e, const char* what) {
-  return mk::set_error(MK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  char buf[320];
+  std::snprintf(buf, sizeof(buf), "%s: %s", what, hipGetErrorString(e));
+  return mk::set_error(MK_ERR_HIP, buf);
 }
 
 #define HIP_TRY(call)                                  \
@@ -196,6 +214,7 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   a.rt[mk::TAG_TOKENS] = (uint64_t)(uintptr_t)tokens;
   a.rt[mk::TAG_POSITIONS] = (uint64_t)(uintptr_t)positions;
   a.rt[mk::TAG_LOGITS] = (uint64_t)(uintptr_t)logits;
+  a.rt[mk::TAG_SCRATCH] = (uint64_t)(uintptr_t)g->scratch;
   a.n_tasks = (uint32_t)g->low.tasks.size();
   a.wait_limit = g->wait_limit;
   a.lvl = g->d_lvl;
@@ -230,6 +249,14 @@ int check_step_args(mk_graph* g, const int32_t* tokens, const int32_t* positions
   return MK_OK;
 }
 
+// The caller's activation workspace, which every step entry point except
+// mk_decode_step_noalloc needs.
+int check_workspace(const mk_graph* g) {
+  if (!g->scratch)
+    return mk::set_error(MK_ERR_INVALID, "graph built without a scratch block: only mk_decode_step_noalloc can run it");
+  return MK_OK;
+}
+
 int reset_state(mk_graph* g, hipStream_t s) {
   const uint32_t n = (uint32_t)g->low.tasks.size();
   const uint32_t blocks = (n + 255) / 256 > 0 ? (n + 255) / 256 : 1;
@@ -240,6 +267,51 @@ int reset_state(mk_graph* g, hipStream_t s) {
   g->ticket_base = 0;
   g->barrier_base = 0;
   g->needs_reset = false;
+  return MK_OK;
+}
+
+// Device address of the static scratch array on device dev (the current device):
+// taken once with hipGetSymbolAddress, then read from the per-device table.
+int static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= mk::kMaxDevices) return mk::set_error(MK_ERR_INVALID, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(mk::scratch_mu);
+  if (!mk::scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(mk::scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return mk::set_error(MK_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    mk::scratch_dev[dev] = p;
+  }
+  *out = mk::scratch_dev[dev];
+  return MK_OK;
+}
+
+// Enqueue one step of g with launch arguments a (per-step buffers resolved): the
+// persistent kernel, or the level-synchronous one.  Allocates nothing.
+int launch_step(mk_graph* g, hipStream_t s, mk::LaunchArgs& a) {
+  int rc;
+  if (g->needs_reset && (rc = reset_state(g, s)) != MK_OK) return rc;
+  a.epoch = g->epoch + 1;
+  a.ticket_base = g->ticket_base;
+  a.barrier_base = g->barrier_base;
+  void* params[] = {&a};
+  if (g->sched_mode == MK_SCHED_LEVELS) {
+    // Counters untouched (the epoch stays): only the barrier counter advances.
+    hipError_t e = hipLaunchCooperativeKernel(g->kernels.levels, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(levels)");
+    g->barrier_base += g->n_lvls * g->grid;
+    g->last_stream = s;
+    return MK_OK;
+  }
+  // Cooperative launch: the runtime refuses the launch (instead of letting the
+  // spinning workgroups deadlock) if the whole grid cannot be resident at once.
+  hipError_t e = hipLaunchCooperativeKernel(g->kernels.persistent, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(interpreter)");
+  g->epoch += 1;
+  // Dynamic mode: every ticket is claimed once and every workgroup makes one failing
+  // claim; static mode leaves the counter alone.
+  if (g->sched_mode == MK_SCHED_DYNAMIC) g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
+  g->last_stream = s;
   return MK_OK;
 }
 
@@ -277,8 +349,8 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
     if (misaligned(weights->dev_ptrs[i], 16))
       return fail(mk::set_error(MK_ERR_ALIGN, "weights: pointer not 16-byte aligned"));
   }
-  if (!scratch_dev) return fail(mk::set_error(MK_ERR_INVALID, "scratch_dev is NULL"));
   if (misaligned(scratch_dev, 256)) return fail(mk::set_error(MK_ERR_ALIGN, "scratch_dev not 256-byte aligned"));
+  g->scratch = scratch_dev;
   g->spec = mk::select_spec(L.cfg);
   if (!g->spec) return fail(mk::set_error(MK_ERR_INVALID, "no kernel specialisation for these dtypes"));
   g->kernels = g->spec->get();
@@ -288,14 +360,22 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, g->device);
   if (e != hipSuccess) return fail(hip_fail(e, "hipGetDeviceProperties"));
+  {
+    // Set-up of mk_decode_step_noalloc on this device: the static scratch array's
+    // address, taken here with the device current so that the step itself calls
+    // nothing but launches.
+    void* unused = nullptr;
+    if ((rc = static_scratch(g->device, &unused)) != MK_OK) return fail(rc);
+  }
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g->kernels.persistent, mk::kThreads, 0);
   if (e != hipSuccess) return fail(hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"));
   if (per_cu < 1) return fail(mk::set_error(MK_ERR_INVALID, "interpreter kernel cannot be resident"));
   g->grid = (uint32_t)prop.multiProcessorCount;  // one workgroup per CU
 
-  // Buffer table: absolute pointers for weights and scratch, tagged offsets for the
-  // per-step buffers (tokens, positions, caches, logits) resolved from launch args.
+  // Buffer table: absolute pointers for weights, tagged offsets for the per-step
+  // buffers (tokens, positions, caches, logits) and for the activations in the
+  // scratch block, resolved from the launch arguments.
   std::vector<uint64_t> table(bi.count(), 0);
   auto W = [&](uint32_t i) { return (uint64_t)(uintptr_t)weights->dev_ptrs[i]; };
   table[bi.tokens()] = (uint64_t)mk::TAG_TOKENS << mk::kTagShift;
@@ -314,7 +394,7 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   table[bi.final_norm()] = W(1 + 6 * nl);
   table[bi.w_lm()] = W(2 + 6 * nl);
   for (uint32_t i = 0; i < bi.count(); ++i)
-    if (L.scratch_off[i] != UINT64_MAX) table[i] = (uint64_t)(uintptr_t)scratch_dev + L.scratch_off[i];
+    if (L.scratch_off[i] != UINT64_MAX) table[i] = ((uint64_t)mk::TAG_SCRATCH << mk::kTagShift) | L.scratch_off[i];
   table[bi.logits()] = (uint64_t)mk::TAG_LOGITS << mk::kTagShift;
 
   // Static schedule over one workgroup per CU.
@@ -457,37 +537,29 @@ int mk_set_trace(mk_graph* g, uint64_t* trace_dev) {
 int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
                    void* kcache_dev, void* vcache_dev, float* logits_dev) {
   int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
-  if (rc) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  if (g->needs_reset && (rc = reset_state(g, s)) != MK_OK) return rc;
+  if (rc || (rc = check_workspace(g))) return rc;
   mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
-  a.epoch = g->epoch + 1;
-  a.ticket_base = g->ticket_base;
-  void* params[] = {&a};
-  if (g->sched_mode == MK_SCHED_LEVELS) {
-    // Counters untouched (the epoch stays): only the barrier counter advances.
-    hipError_t e = hipLaunchCooperativeKernel(g->kernels.levels, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
-    if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(levels)");
-    g->barrier_base += g->n_lvls * g->grid;
-    g->last_stream = s;
-    return MK_OK;
-  }
-  // Cooperative launch: the runtime refuses the launch (instead of letting the
-  // spinning workgroups deadlock) if the whole grid cannot be resident at once.
-  hipError_t e = hipLaunchCooperativeKernel(g->kernels.persistent, dim3(g->grid), dim3(mk::kThreads), params, 0, s);
-  if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(interpreter)");
-  g->epoch += 1;
-  // Dynamic mode: every ticket is claimed once and every workgroup makes one failing
-  // claim; static mode leaves the counter alone.
-  if (g->sched_mode == MK_SCHED_DYNAMIC) g->ticket_base += (uint32_t)g->low.tasks.size() + g->grid;
-  g->last_stream = s;
-  return MK_OK;
+  return launch_step(g, (hipStream_t)stream, a);
+}
+
+int mk_decode_step_noalloc(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
+                           void* kcache_dev, void* vcache_dev, float* logits_dev) {
+  int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  if (rc) return rc;
+  if (g->low.scratch_total > mk::kStaticScratchBytes)
+    return mk::set_error(MK_ERR_INVALID,
+                         "the step's activations exceed the 64 MiB static scratch array (mk_plan scratch_bytes)");
+  void* p = nullptr;
+  if ((rc = static_scratch(g->device, &p)) != MK_OK) return rc;
+  mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+  a.rt[mk::TAG_SCRATCH] = (uint64_t)(uintptr_t)p;
+  return launch_step(g, (hipStream_t)stream, a);
 }
 
 int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
                           void* kcache_dev, void* vcache_dev, float* logits_dev) {
   int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
-  if (rc) return rc;
+  if (rc || (rc = check_workspace(g))) return rc;
   hipStream_t s = (hipStream_t)stream;
   mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
   a.trace = nullptr;
@@ -546,7 +618,7 @@ void drop_per_op_graph(mk_graph* g) {
 int mk_capture_per_op_graph(mk_graph* g, const int32_t* tokens_dev, const int32_t* positions_dev,
                             void* kcache_dev, void* vcache_dev, float* logits_dev) {
   int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
-  if (rc) return rc;
+  if (rc || (rc = check_workspace(g))) return rc;
   drop_per_op_graph(g);
   hipStream_t cs = nullptr;
   HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
