@@ -33,12 +33,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_layers=(1, 2), min_seconds=6.0):
+def blas_threads() -> tuple[int, int]:
+    """(threads for the oracle's BLAS, cores this process may run on): every core of
+    the affinity mask, capped by OMP_NUM_THREADS when the environment sets it (the
+    host's share of CPUs for one GPU)."""
+    affinity = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cap = int(env) if env.isdigit() and int(env) > 0 else affinity
+    return min(affinity, cap), affinity
+
+
+def cpu_baseline(w, layer_counts=(1, 2, 3), min_seconds=5.0):
     """The oracle (float64 numpy) timed on this host on a bounded sample: the full step
-    with 1 and with 2 layers (same shapes, weights generated beforehand), each repeated
-    until about min_seconds of oracle work is timed (median per step), extrapolated
-    linearly to the workload's layer count."""
-    from threadpoolctl import threadpool_info
+    of the same shapes with 1, 2 and 3 layers (weights generated beforehand), each
+    repeated until about min_seconds of oracle work is timed (median per step); a
+    least-squares line through the three medians is extrapolated to the workload's
+    layer count.  The spread of the per-layer slope between pairs of samples is
+    reported with it."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import decode as od
     from oracle.params import GeneratedParams
@@ -60,38 +72,42 @@ def cpu_baseline(w, budget_layers=(1, 2), min_seconds=6.0):
         def cache(self, *a):
             return self.p.cache(*a)
 
+    threads, affinity = blas_threads()
     times, reps = {}, {}
-    for nl in budget_layers:
-        ws = w.replace(n_layers=nl)
-        p = GeneratedParams(ws, backend="c")
-        mats = [s[0] for s in ws.weight_specs() if len(s[2]) == 2 and s[1] != "embedding"]
-        pre = Pregenerated(p, mats)
-        kv = od.KVState(pre)
-        # warm the cache generator too: time only the oracle's arithmetic
-        for l in range(nl):
-            for b in range(ws.batch):
-                for g in range(ws.n_kv_heads):
-                    for which in (0, 1):
-                        pre.p.cache(l, which, b, g, 1)
-        # repeat the step until about min_seconds of oracle work is timed; median
-        runs = []
-        while sum(runs) < min_seconds or len(runs) < 3:
-            t0 = time.perf_counter()
-            od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
-            runs.append(time.perf_counter() - t0)
-        times[nl] = float(np.median(runs))
-        reps[nl] = len(runs)
-        del pre, kv
-    per_layer = times[2] - times[1]
-    fixed = times[1] - per_layer
-    est = fixed + w.n_layers * per_layer
-    blas = [i.get("num_threads", 1) for i in threadpool_info()]
-    cores = max([1] + blas)
-    return {"value": w.batch / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float64 numpy oracle, full step of the same shapes with 1 layer (median {times[1]:.3f} s "
-                       f"of {reps[1]} runs) and 2 layers (median {times[2]:.3f} s of {reps[2]} runs), "
-                       f"extrapolated to {w.n_layers} layers = {est:.2f} s/step"),
-            "seconds_per_step_estimate": est}
+    with threadpool_limits(limits=threads):
+        used = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+        for nl in layer_counts:
+            ws = w.replace(n_layers=nl)
+            p = GeneratedParams(ws, backend="c")
+            mats = [s[0] for s in ws.weight_specs() if len(s[2]) == 2 and s[1] != "embedding"]
+            pre = Pregenerated(p, mats)
+            kv = od.KVState(pre)
+            # warm the cache generator too: time only the oracle's arithmetic
+            for l in range(nl):
+                for b in range(ws.batch):
+                    for g in range(ws.n_kv_heads):
+                        for which in (0, 1):
+                            pre.p.cache(l, which, b, g, 1)
+            runs = []
+            while sum(runs) < min_seconds or len(runs) < 3:
+                t0 = time.perf_counter()
+                od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
+                runs.append(time.perf_counter() - t0)
+            times[nl] = float(np.median(runs))
+            reps[nl] = len(runs)
+            del pre, kv
+    xs = np.array(layer_counts, dtype=np.float64)
+    ys = np.array([times[n] for n in layer_counts])
+    per_layer, fixed = np.polyfit(xs, ys, 1)
+    slopes = [(times[b] - times[a]) / (b - a) for i, a in enumerate(layer_counts) for b in layer_counts[i + 1:]]
+    est = float(fixed + w.n_layers * per_layer)
+    samples = ", ".join(f"{n} layer{'s' if n > 1 else ''} median {times[n]:.3f} s of {reps[n]} runs"
+                        for n in layer_counts)
+    return {"value": w.batch / est, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": (f"float64 numpy oracle, full step of the same shapes with {samples}; least-squares "
+                       f"line extrapolated to {w.n_layers} layers = {est:.2f} s/step (per-layer slope "
+                       f"{per_layer:.4f} s, pairwise slopes {min(slopes):.4f}-{max(slopes):.4f} s)"),
+            "affinity_cores": affinity, "seconds_per_step_estimate": est}
 
 
 KERNEL_SRC = os.path.join(ROOT, "task_graph_interpreter_amd", "csrc")
@@ -203,12 +219,84 @@ def greedy_run(w, inp, n_tokens, stream):
                     "each step followed by the SAMPLE kernel (argmax and position update), no host round trip"}
 
 
+def timed(fn, steps, warmup, stream, ptrs):
+    """Run fn(stream, *ptrs) warmup times, then time steps calls with HIP events on the
+    stream the kernels run on.  Returns (total ms, per-call ms array)."""
+    import torch
+
+    for _ in range(warmup):
+        fn(stream, *ptrs)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn(stream, *ptrs)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return ev[0].elapsed_time(ev[steps]), per
+
+
+def model_key(w):
+    """Workloads with equal keys have bitwise-equal weights (same shapes and seed)."""
+    return (w.n_layers, w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.intermediate, w.vocab, w.weight_dtype,
+            w.seed)
+
+
+def time_other_workload(name, steps, warmup, stream, shared):
+    """Another workload timed in the same run: the persistent step and the per-op
+    launches of the same graph, after checking that both give the same logits within
+    the parity tolerance.  ``shared`` = (model_key, weight tensors) of a workload
+    already on the device, reused when the model is the same."""
+    import torch
+
+    import task_graph_interpreter_amd as mk
+    from synth import workloads
+    from synth.device import DeviceInputs
+
+    w = workloads.get(name)
+    reuse = shared is not None and shared[0] == model_key(w)
+    log(f"{name}: filling inputs" + (" (weights shared)" if reuse else ""))
+    inp = DeviceInputs(w, weights=shared[1] if reuse else None)
+    cfg, keep = mk.make_cfg(**w.mk_fields())
+    plan = mk.mk_plan(cfg)
+    scratch = torch.zeros(plan["scratch_bytes"], dtype=torch.uint8, device="cuda")
+    g = mk.mk_build_graph(cfg, inp.weight_ptrs(), scratch.data_ptr(), stream)
+    ptrs = inp.step_ptrs()
+    g.mk_decode_step(stream, *ptrs)
+    assert g.mk_status() == 0
+    mega = inp.logits.clone()
+    g.mk_decode_step_per_op(stream, *ptrs)
+    torch.cuda.synchronize()
+    diff = (inp.logits - mega).abs().max().item()
+    assert diff <= 2e-2, f"{name}: per-op and persistent logits differ by {diff}"
+    total, per = timed(g.mk_decode_step, steps, warmup, stream, ptrs)
+    assert g.mk_status() == 0
+    t2, _ = timed(g.mk_decode_step_per_op, steps, warmup, stream, ptrs)
+    ms, ms2 = total / steps, t2 / steps
+    achieved = w.bytes_per_step() / (ms / 1e3) / 1e9
+    out = {"workload": name, "batch": w.batch, "kv_len": list(w.kv_len), "kv_chunk": w.kv_chunk,
+           "gemv_config": w.gemv_config, "kernel": g.mk_graph_kernel_name(), "ms_per_step": ms,
+           "latency_ms_median": float(np.median(per)), "tokens_per_s": w.batch * steps / (total / 1e3),
+           "bytes_per_step": w.bytes_per_step(), "achieved_gbs": achieved, "frac": achieved / PEAK_HBM_GBS,
+           "traffic": measured_traffic(name), "per_op_ms_per_step": ms2, "speedup_over_per_op": ms2 / ms}
+    log(f"{name}: persistent {ms:.4f} ms/step ({achieved:.0f} GB/s, {achieved / PEAK_HBM_GBS:.3f} of peak), "
+        f"per-op {ms2:.4f} ms/step")
+    g.close()
+    del inp, scratch, keep
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="8b_b1")
+    ap.add_argument("--others", default="1b_b1,8b_b8_ragged,8b_b32_32k",
+                    help="comma-separated workloads also timed in this run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
     ap.add_argument("--no-alt-schedule", action="store_true", help="skip timing the other schedule mode")
@@ -295,21 +383,7 @@ def main():
         assert diff <= 2e-2, f"per-op and persistent logits differ by {diff}"
     log(f"graph: {plan['n_tasks']} tasks, {plan['n_edges']} edges, {plan['n_levels']} levels, grid {g.mk_graph_grid()}")
 
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn(stream, *ptrs)
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record()
-        for i in range(steps):
-            fn(stream, *ptrs)
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-        total = ev[0].elapsed_time(ev[steps])
-        return total, per
-
-    total, per = timed(g.mk_decode_step, args.steps, args.warmup)
+    total, per = timed(g.mk_decode_step, args.steps, args.warmup, stream, ptrs)
     assert g.mk_status() == 0
     ms = total / args.steps
     tok_s = w.batch * args.steps / (total / 1e3)
@@ -350,7 +424,7 @@ def main():
             g.mk_decode_step(stream, *ptrs)
             assert g.mk_status() == 0
             assert torch.equal(inp.logits, ref_logits), f"{other} schedule differs from {args.schedule}"
-            t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup)
+            t_alt, _ = timed(g.mk_decode_step, args.steps, args.warmup, stream, ptrs)
             assert g.mk_status() == 0
             alt.append({"schedule": other, "ms_per_step": t_alt / args.steps})
             log(f"persistent, {other} schedule: {t_alt / args.steps:.4f} ms/step")
@@ -358,7 +432,7 @@ def main():
 
     per_op = None
     if not args.no_per_op:
-        t2, per2 = timed(g.mk_decode_step_per_op, args.steps, args.warmup)
+        t2, per2 = timed(g.mk_decode_step_per_op, args.steps, args.warmup, stream, ptrs)
         ms2 = t2 / args.steps
         per_op = {"ms_per_step": ms2, "value": w.batch * args.steps / (t2 / 1e3), "unit": "tokens/s",
                   "launches_per_step": 2 + 7 * w.n_layers,
@@ -377,7 +451,7 @@ def main():
         assert g.mk_status() == 0
         torch.cuda.synchronize()
         assert torch.equal(inp.logits, eager), "graph replay of the per-op launches differs from the eager step"
-        t3, per3 = timed(lambda s, *p: g.mk_launch_per_op_graph(s), args.steps, args.warmup)
+        t3, per3 = timed(lambda s, *p: g.mk_launch_per_op_graph(s), args.steps, args.warmup, stream, ptrs)
         assert g.mk_status() == 0
         per_op["graph_replay"] = {"ms_per_step": t3 / args.steps, "latency_ms_median": float(np.median(per3)),
                                   "speedup_of_persistent": (t3 / args.steps) / ms}
@@ -397,11 +471,23 @@ def main():
         with open(args.trace_out.replace(".npy", "_summary.json"), "w") as f:
             json.dump(summary, f, indent=1)
         log("trace summary:\n" + mktrace.format_summary(summary))
+        del tr
 
     n_greedy = args.greedy_tokens if args.greedy_tokens >= 0 else (256 if w.batch == 1 else 0)
     greedy = greedy_run(w, inp, n_greedy, stream) if n_greedy > 0 else None
 
     traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles or args.gemv_config >= 0) else None
+    name_timed = g.mk_graph_kernel_name()
+    g.close()
+    del scratch
+
+    others = []
+    shared = (model_key(w), inp.weights)
+    for name in [n for n in args.others.split(",") if n and n != w.name]:
+        others.append(time_other_workload(name, args.steps, args.warmup, stream, shared))
+    del shared, inp, ptrs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -426,7 +512,8 @@ def main():
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "intermediate": w.intermediate,
                    "vocab": w.vocab, "batch": w.batch, "kv_len": list(w.kv_len)[:4], "weight_dtype": w.weight_dtype,
                    "kv_dtype": w.kv_dtype, "gemv_tiles": w.gemv_tiles, "kv_chunk": w.kv_chunk,
-                   "tasks": plan["n_tasks"], "edges": plan["n_edges"], "schedule": args.schedule},
+                   "tasks": plan["n_tasks"], "edges": plan["n_edges"], "schedule": args.schedule,
+                   "kernel": name_timed},
         "latency_ms": {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
                        "p90": float(np.percentile(per, 90))},
         "bytes_per_step": bytes_step,
@@ -436,9 +523,9 @@ def main():
         "other_schedule": alt,
         "stream_ceiling": stream_ceiling,
         "greedy": greedy,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
-    g.close()
     print(json.dumps(out), flush=True)
 
 
