@@ -43,13 +43,14 @@ def blas_threads() -> tuple[int, int]:
     return min(affinity, cap), affinity
 
 
-def cpu_baseline(w, layer_counts=(1, 2, 3), min_seconds=5.0):
+def cpu_baseline(w, layer_counts=(1, 2, 3), min_seconds=12.0):
     """The oracle (float64 numpy) timed on this host on a bounded sample: the full step
-    of the same shapes with 1, 2 and 3 layers (weights generated beforehand), each
-    repeated until about min_seconds of oracle work is timed (median per step); a
-    least-squares line through the three medians is extrapolated to the workload's
-    layer count.  The spread of the per-layer slope between pairs of samples is
-    reported with it."""
+    of the same shapes with 1, 2 and 3 layers.  Weights and the cache slices the step
+    reads are generated beforehand, so only the oracle's arithmetic is timed.  The
+    three variants run round robin until about min_seconds of oracle work is timed
+    (slow drifts of the host then hit all three alike); a least-squares line through
+    the three medians is extrapolated to the workload's layer count, and the spread of
+    the per-layer slope between pairs of samples is reported with it."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import decode as od
@@ -59,6 +60,7 @@ def cpu_baseline(w, layer_counts=(1, 2, 3), min_seconds=5.0):
         def __init__(self, p, tids):
             self.p = p
             self.m = {t: p.matrix(t) for t in tids}
+            self.c = {}
 
         def embedding_row(self, tok):
             return self.p.embedding_row(tok)
@@ -70,43 +72,42 @@ def cpu_baseline(w, layer_counts=(1, 2, 3), min_seconds=5.0):
             return self.m[tid]
 
         def cache(self, *a):
-            return self.p.cache(*a)
+            if a not in self.c:
+                self.c[a] = self.p.cache(*a)
+            return self.c[a]
 
     threads, affinity = blas_threads()
-    times, reps = {}, {}
+    runs = {n: [] for n in layer_counts}
     with threadpool_limits(limits=threads):
         used = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+        variants = {}
         for nl in layer_counts:
             ws = w.replace(n_layers=nl)
             p = GeneratedParams(ws, backend="c")
             mats = [s[0] for s in ws.weight_specs() if len(s[2]) == 2 and s[1] != "embedding"]
             pre = Pregenerated(p, mats)
-            kv = od.KVState(pre)
-            # warm the cache generator too: time only the oracle's arithmetic
-            for l in range(nl):
-                for b in range(ws.batch):
-                    for g in range(ws.n_kv_heads):
-                        for which in (0, 1):
-                            pre.p.cache(l, which, b, g, 1)
-            runs = []
-            while sum(runs) < min_seconds or len(runs) < 3:
+            od.decode_step(ws, pre, ws.tokens(), ws.positions(), od.KVState(pre))  # fills the cache slices
+            variants[nl] = (ws, pre)
+        while sum(sum(r) for r in runs.values()) < min_seconds or min(len(r) for r in runs.values()) < 3:
+            for nl in layer_counts:
+                ws, pre = variants[nl]
+                kv = od.KVState(pre)
                 t0 = time.perf_counter()
                 od.decode_step(ws, pre, ws.tokens(), ws.positions(), kv)
-                runs.append(time.perf_counter() - t0)
-            times[nl] = float(np.median(runs))
-            reps[nl] = len(runs)
-            del pre, kv
+                runs[nl].append(time.perf_counter() - t0)
+        del variants
+    times = {n: float(np.median(r)) for n, r in runs.items()}
     xs = np.array(layer_counts, dtype=np.float64)
     ys = np.array([times[n] for n in layer_counts])
     per_layer, fixed = np.polyfit(xs, ys, 1)
     slopes = [(times[b] - times[a]) / (b - a) for i, a in enumerate(layer_counts) for b in layer_counts[i + 1:]]
     est = float(fixed + w.n_layers * per_layer)
-    samples = ", ".join(f"{n} layer{'s' if n > 1 else ''} median {times[n]:.3f} s of {reps[n]} runs"
+    samples = ", ".join(f"{n} layer{'s' if n > 1 else ''} median {times[n]:.3f} s of {len(runs[n])} runs"
                         for n in layer_counts)
     return {"value": w.batch / est, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": (f"float64 numpy oracle, full step of the same shapes with {samples}; least-squares "
-                       f"line extrapolated to {w.n_layers} layers = {est:.2f} s/step (per-layer slope "
-                       f"{per_layer:.4f} s, pairwise slopes {min(slopes):.4f}-{max(slopes):.4f} s)"),
+            "sample": (f"float64 numpy oracle, full step of the same shapes with {samples}, run round robin; "
+                       f"least-squares line extrapolated to {w.n_layers} layers = {est:.2f} s/step (per-layer "
+                       f"slope {per_layer:.4f} s, pairwise slopes {min(slopes):.4f}-{max(slopes):.4f} s)"),
             "affinity_cores": affinity, "seconds_per_step_estimate": est}
 
 
