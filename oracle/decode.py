@@ -117,7 +117,10 @@ def decode_step(w, params, tokens, positions, kv: KVState, rows=None, keep: bool
 
     Returns (logits[len(rows), vocab], inter) where ``inter`` (if ``keep``) maps
     activation names to per-row float64 arrays, using the names of the step's
-    activation buffers (x0, and per layer qkv_out, q_rot, partials, att, h, gu, x_out).
+    activation buffers (x0, and per layer qkv_out, q_rot, partials, att, h, gu, x_out),
+    plus the values a graph lowered without epilogue fusion also stores: per layer xn
+    (normed attention input), o (o projection before the residual), hn (normed MLP
+    input), d (down projection before the residual), and xn_final.
     With ``split`` the attention is computed chunk by chunk and merged (the lowered
     form); otherwise by the plain softmax definition.
     """
@@ -168,7 +171,8 @@ def decode_step(w, params, tokens, positions, kv: KVState, rows=None, keep: bool
                     else:
                         att[r, h * hd:(h + 1) * hd] = softmax_attention(qr[h], K, V)
         Wo = params.matrix(w.tid_layer(l, 2))
-        h_res = x + att @ Wo.T
+        o_proj = att @ Wo.T
+        h_res = x + o_proj
         del Wo
         g_mlp = params.vector(w.tid_layer(l, 3))
         Wgu = params.matrix(w.tid_layer(l, 4))
@@ -177,9 +181,14 @@ def decode_step(w, params, tokens, positions, kv: KVState, rows=None, keep: bool
         del Wgu
         gu = silu(z[:, :I]) * z[:, I:]
         Wd = params.matrix(w.tid_layer(l, 5))
-        x_out = h_res + gu @ Wd.T
+        d_proj = gu @ Wd.T
+        x_out = h_res + d_proj
         del Wd
         if keep:
+            inter[f"l{l}.xn"] = xn
+            inter[f"l{l}.o"] = o_proj
+            inter[f"l{l}.hn"] = hn
+            inter[f"l{l}.d"] = d_proj
             inter[f"l{l}.qkv_out"] = qkv
             inter[f"l{l}.q_rot"] = q_rot
             inter[f"l{l}.partials"] = partials
@@ -191,6 +200,8 @@ def decode_step(w, params, tokens, positions, kv: KVState, rows=None, keep: bool
     g_fin = params.vector(w.tid_final_norm)
     Wlm = params.matrix(w.tid_lm)
     xn = np.stack([rmsnorm(x[r], g_fin, eps) for r in range(len(rows))])
+    if keep:
+        inter["xn_final"] = xn
     logits = xn @ Wlm.T
     return logits, inter
 

@@ -27,11 +27,25 @@ builders follow):
      prefix sum of num_dependents; edges are uint32 child indices.
   R9 joins: for an op with >= 2 tasks whose tasks share >= 2 parents S, a NOP with
      parents S is emitted and each task's parents become (own - S) + {NOP}.
+  R10 the step is first written as a list of ops, the way the page's graph API builds
+     it (embed, rmsnorm, matmul, attention, and sample for a greedy step).  Written
+     without fusion, every RMSNorm is its own op and each residual add rides on the
+     next RMSNorm (the FUSED_RESIDUAL flag of the descriptor section: the norm also
+     writes the sum).  The epilogue-fusion pass the page names as future work (graph
+     API section) then folds each residual add into the matmul that produced the
+     summand (ADD_RESIDUAL) and each RMSNorm read only by matmuls into those matmuls
+     (RMS_NORM_INPUT); the result is the hand-fused decoder of the graph-API section.
+  R11 RMSNORM (OpId 3) is one task per batch row (the norm needs the whole row); SAMPLE
+     (OpId 6) is one task per batch row after the lm_head, writing the row's greedy
+     token and advancing its position.
 Parity: pinned by the page's worked tiling example (3072 columns in 8 tiles of 384),
 the descriptor layout and OpId/flag values printed on the page, and by the invariants
 in ``check_graph`` (topological order, read-after-write coverage, in-degrees, SSA).
 """
 from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -49,21 +63,27 @@ assert TASK_DTYPE.itemsize == 64
 NOP, MEMCPY, GEMV, RMSNORM, ATTENTION, MLP, SAMPLE, APPEND, PARTIAL, COMBINE = range(10)
 # Flag bits of the page.
 SILU_MUL, ADD_RESIDUAL, RMS_NORM_INPUT = 1, 2, 4
+FUSED_RESIDUAL = 2  # the same bit on an RMSNORM descriptor
 NONE = 0xFFFF
 
 
 class BufferIndex:
-    """Canonical buffer-table indices (append-only order)."""
+    """Canonical buffer-table indices (append-only order).  A graph lowered without
+    epilogue fusion has five more activation buffers per layer group, appended after
+    the logits: per layer the normed attention input, the o-projection output, the
+    normed MLP input and the down-projection output, then the normed final input."""
 
     def __init__(self, w):
         L = w.n_layers
+        self.L = L
         self.tokens, self.positions, self.embedding = 0, 1, 2
         self.final_norm = 3 + 8 * L
         self.w_lm = 4 + 8 * L
         self.scratch0 = 5 + 8 * L
         self.x0 = self.scratch0
         self.logits = self.scratch0 + 1 + 7 * L
-        self.count = self.logits + 1
+        self.unfused = bool(getattr(w, "unfused", 0))
+        self.count = self.logits + 1 + ((4 * L + 1) if self.unfused else 0)
 
     @staticmethod
     def layer(l, which):
@@ -72,6 +92,12 @@ class BufferIndex:
     def act(self, l, which):
         """which: 0 qkv_out, 1 q_rot, 2 partials, 3 att, 4 h, 5 gu, 6 x_out."""
         return self.scratch0 + 1 + 7 * l + which
+
+    def extra(self, l, which):
+        """Unfused graphs only.  which: 0 xn (normed attention input), 1 o (o-projection
+        output), 2 hn (normed MLP input), 3 d (down-projection output); l = n_layers,
+        which 0: the normed final input."""
+        return self.logits + 1 + 4 * l + which
 
 
 def tile_bounds(N: int, T: int, mfma: bool):
@@ -123,11 +149,139 @@ def validate(w) -> None:
         raise ValueError("more than 65535 buffers")
 
 
-def build_graph(w):
-    """Lower one decode step of workload ``w``; returns (tasks[TASK_DTYPE], edges[uint32])."""
-    validate(w)
+EMBED, NORM, MATMUL, ATTN, SAMPLE_OP = "embed", "rmsnorm", "matmul", "attention", "sample"
+
+
+@dataclass(frozen=True)
+class Op:
+    """One op of the step as the graph API builds it, before the fan-out into tasks.
+    matmul: out = x W^T, with gamma (RMS_NORM_INPUT: x is normed first), residual
+    (ADD_RESIDUAL) and silu (SILU_MUL) as its epilogue flags.  rmsnorm: out =
+    rmsnorm(x [+ residual]) * gamma, writing the sum x + residual to out2 when there
+    is a residual (FUSED_RESIDUAL).  attention: layer ``layer`` from its qkv input x.
+    embed: x0 from the tokens.  sample: greedy token of each row of x."""
+    kind: str
+    out: int
+    x: int = NONE
+    w: int = NONE
+    gamma: int = NONE
+    residual: int = NONE
+    out2: int = NONE
+    silu: bool = False
+    K: int = 0
+    N: int = 0
+    layer: int = -1
+
+
+def decoder_program(w):
+    """The decode step written with the graph API and no fusion: every RMSNorm its
+    own op, each residual add carried by the next RMSNorm (FUSED_RESIDUAL)."""
+    bi = BufferIndex(w.replace(unfused=1))
+    H, I, V, L = w.hidden, w.intermediate, w.vocab, w.n_layers
+    ops = [Op(EMBED, bi.x0, x=bi.tokens, w=bi.embedding)]
+    x_in = bi.x0
+    for l in range(L):
+        qkv, _, _, att, h, gu, xo = (bi.act(l, j) for j in range(7))
+        xn, o, hn, d = (bi.extra(l, j) for j in range(4))
+        if l == 0:
+            ops.append(Op(NORM, xn, x=bi.x0, gamma=bi.layer(0, 0), N=H))
+        else:  # the previous layer's residual add rides on this norm
+            ops.append(Op(NORM, xn, x=bi.extra(l - 1, 3), gamma=bi.layer(l, 0), residual=bi.act(l - 1, 4),
+                          out2=x_in, N=H))
+        ops.append(Op(MATMUL, qkv, x=xn, w=bi.layer(l, 1), K=H, N=w.qkv_cols))
+        ops.append(Op(ATTN, att, x=qkv, layer=l))
+        ops.append(Op(MATMUL, o, x=att, w=bi.layer(l, 2), K=w.q_cols, N=H))
+        ops.append(Op(NORM, hn, x=o, gamma=bi.layer(l, 3), residual=x_in, out2=h, N=H))
+        ops.append(Op(MATMUL, gu, x=hn, w=bi.layer(l, 4), silu=True, K=H, N=I))
+        ops.append(Op(MATMUL, d, x=gu, w=bi.layer(l, 5), K=I, N=H))
+        x_in = xo
+    xf = bi.extra(L, 0)
+    ops.append(Op(NORM, xf, x=bi.extra(L - 1, 3), gamma=bi.final_norm, residual=bi.act(L - 1, 4), out2=x_in, N=H))
+    ops.append(Op(MATMUL, bi.logits, x=xf, w=bi.w_lm, K=H, N=V))
+    return ops
+
+
+def hand_fused_program(w):
+    """The decoder as the graph-API section writes it, fusions given by hand: norm and
+    residual as kwargs of the matmuls, the final norm inside the lm_head matmul."""
     bi = BufferIndex(w)
-    B, H, hd, Hq, Hkv, I, V = w.batch, w.hidden, w.head_dim, w.n_q_heads, w.n_kv_heads, w.intermediate, w.vocab
+    H, I, V = w.hidden, w.intermediate, w.vocab
+    ops = [Op(EMBED, bi.x0, x=bi.tokens, w=bi.embedding)]
+    x = bi.x0
+    for l in range(w.n_layers):
+        qkv, _, _, att, h, gu, xo = (bi.act(l, j) for j in range(7))
+        ops.append(Op(MATMUL, qkv, x=x, w=bi.layer(l, 1), gamma=bi.layer(l, 0), K=H, N=w.qkv_cols))
+        ops.append(Op(ATTN, att, x=qkv, layer=l))
+        ops.append(Op(MATMUL, h, x=att, w=bi.layer(l, 2), residual=x, K=w.q_cols, N=H))
+        ops.append(Op(MATMUL, gu, x=h, w=bi.layer(l, 4), gamma=bi.layer(l, 3), silu=True, K=H, N=I))
+        ops.append(Op(MATMUL, xo, x=gu, w=bi.layer(l, 5), residual=h, K=I, N=H))
+        x = xo
+    ops.append(Op(MATMUL, bi.logits, x=x, w=bi.w_lm, gamma=bi.final_norm, K=H, N=V))
+    return ops
+
+
+def fuse_epilogues(ops):
+    """The automatic epilogue-fusion pass over an op list.
+      1. rmsnorm(m, gamma, residual r) -> (y, sum s), where m is written by a matmul
+         with no epilogue and read by nothing else: the matmul adds r itself
+         (ADD_RESIDUAL) and writes s; the norm then reads s with no residual.
+      2. rmsnorm(x, gamma) -> y with no residual, where every reader of y is a matmul
+         with neither an input norm nor a residual (one gamma/residual slot per
+         descriptor): each reader reads x with RMS_NORM_INPUT gamma, and the norm op
+         is dropped.
+    Anything else stays as it is."""
+    ops = list(ops)
+
+    def readers(buf):
+        return [i for i, o in enumerate(ops) if o is not None and buf in (o.x, o.residual)]
+
+    def writer(buf):
+        return [i for i, o in enumerate(ops) if o is not None and buf in (o.out, o.out2)]
+
+    for i, o in enumerate(ops):
+        if o.kind != NORM or o.residual == NONE:
+            continue
+        wr = writer(o.x)
+        if len(wr) != 1 or readers(o.x) != [i]:
+            continue
+        m = ops[wr[0]]
+        if m.kind != MATMUL or m.gamma != NONE or m.residual != NONE or m.silu:
+            continue
+        ops[wr[0]] = dataclasses.replace(m, residual=o.residual, out=o.out2)
+        ops[i] = dataclasses.replace(o, x=o.out2, residual=NONE, out2=NONE)
+    for i, o in enumerate(ops):
+        if o is None or o.kind != NORM or o.residual != NONE:
+            continue
+        rs = readers(o.out)
+        if not rs or any(ops[r].kind != MATMUL or ops[r].x != o.out or ops[r].gamma != NONE
+                         or ops[r].residual != NONE for r in rs):
+            continue
+        for r in rs:
+            ops[r] = dataclasses.replace(ops[r], x=o.x, gamma=o.gamma)
+        ops[i] = None
+    return [o for o in ops if o is not None]
+
+
+def step_program(w):
+    """The op list build_graph lowers: the decoder program, through the fusion pass
+    unless the workload asks for the unfused graph, plus the sample op for a greedy
+    step."""
+    ops = decoder_program(w)
+    if not getattr(w, "unfused", 0):
+        ops = fuse_epilogues(ops)
+    if getattr(w, "sample", 0):
+        bi = BufferIndex(w)
+        ops.append(Op(SAMPLE_OP, bi.tokens, x=bi.logits, out2=bi.positions, N=w.vocab))
+    return ops
+
+
+def build_graph(w, program=None):
+    """Lower one decode step of workload ``w`` (the op list of step_program, or
+    ``program``); returns (tasks[TASK_DTYPE], edges[uint32])."""
+    validate(w)
+    ops = step_program(w) if program is None else program
+    bi = BufferIndex(w)
+    B, H, hd, Hq, Hkv, I = w.batch, w.hidden, w.head_dim, w.n_q_heads, w.n_kv_heads, w.intermediate
     grp, T, mfma = Hq // Hkv, w.gemv_tiles, w.gemv_config == 2
     C = [w.chunks(b) for b in range(B)]
     base = {}
@@ -163,25 +317,39 @@ def build_graph(w):
             for rect in wr:
                 writers.add(*rect, idx)
 
-    def gemv_op(x, K, W, N, flags, aux, y):
+    def gemv_op(o):
+        flags = (RMS_NORM_INPUT if o.gamma != NONE else 0) | (ADD_RESIDUAL if o.residual != NONE else 0) | \
+                (SILU_MUL if o.silu else 0)
+        aux = o.gamma if o.gamma != NONE else o.residual
         specs = []
-        for (c0, c1) in tile_bounds(N, T, mfma):
-            f = dict(op_id=GEMV, config_id=w.gemv_config, flags=flags, m=B, n=N, k=K,
-                     in_buf=(x, W, aux), out_buf=y,
-                     reserved=(c0, c1 - c0, I if flags & SILU_MUL else 0, 0, 0))
-            reads = [(x, 0, B, 0, K)]
-            if flags & ADD_RESIDUAL:
-                reads.append((aux, 0, B, c0, c1))
-            specs.append((f, reads, [(y, 0, B, c0, c1)]))
+        for (c0, c1) in tile_bounds(o.N, T, mfma):
+            f = dict(op_id=GEMV, config_id=w.gemv_config, flags=flags, m=B, n=o.N, k=o.K,
+                     in_buf=(o.x, o.w, aux), out_buf=o.out,
+                     reserved=(c0, c1 - c0, I if o.silu else 0, 0, 0))
+            reads = [(o.x, 0, B, 0, o.K)]
+            if o.residual != NONE:
+                reads.append((o.residual, 0, B, c0, c1))
+            specs.append((f, reads, [(o.out, 0, B, c0, c1)]))
         emit_op(specs)
 
-    emit_op([(dict(op_id=MEMCPY, config_id=_dtype_code(w.weight_dtype), m=B, n=H, k=0,
-                   in_buf=(bi.tokens, bi.embedding, NONE), out_buf=bi.x0), [], [(bi.x0, 0, B, 0, H)])])
-    x = bi.x0
-    for l in range(w.n_layers):
-        qkv, qrot, part, att, hbuf, gu, xo = (bi.act(l, j) for j in range(7))
+    def norm_op(o):
+        specs = []
+        for b in range(B):
+            f = dict(op_id=RMSNORM, config_id=_dtype_code(w.weight_dtype),
+                     flags=FUSED_RESIDUAL if o.residual != NONE else 0, m=B, n=o.N, k=0,
+                     in_buf=(o.x, o.gamma, o.residual), out_buf=o.out, reserved=(b, o.out2, 0, 0, 0))
+            reads = [(o.x, b, b + 1, 0, o.N)]
+            writes = [(o.out, b, b + 1, 0, o.N)]
+            if o.residual != NONE:
+                reads.append((o.residual, b, b + 1, 0, o.N))
+                writes.append((o.out2, b, b + 1, 0, o.N))
+            specs.append((f, reads, writes))
+        emit_op(specs)
+
+    def attention_ops(o):
+        l, qkv, att = o.layer, o.x, o.out
+        qrot, part = bi.act(l, 1), bi.act(l, 2)
         kc, vc = bi.layer(l, 6), bi.layer(l, 7)
-        gemv_op(x, H, bi.layer(l, 1), w.qkv_cols, RMS_NORM_INPUT, bi.layer(l, 0), qkv)
         kvc = _dtype_code(w.kv_dtype)
         specs = []
         for b in range(B):
@@ -213,11 +381,29 @@ def build_graph(w):
                          in_buf=(part, NONE, NONE), out_buf=att, reserved=(b, g * grp, grp, 0, bs))
                 specs.append((f, [(part, 0, 1, bs, bs + C[b])], [(att, b, b + 1, q0, q1)]))
         emit_op(specs)
-        gemv_op(att, Hq * hd, bi.layer(l, 2), H, ADD_RESIDUAL, x, hbuf)
-        gemv_op(hbuf, H, bi.layer(l, 4), I, RMS_NORM_INPUT | SILU_MUL, bi.layer(l, 3), gu)
-        gemv_op(gu, I, bi.layer(l, 5), H, ADD_RESIDUAL, hbuf, xo)
-        x = xo
-    gemv_op(x, H, bi.w_lm, V, RMS_NORM_INPUT, bi.final_norm, bi.logits)
+
+    def sample_op(o):
+        specs = []
+        for b in range(B):
+            f = dict(op_id=SAMPLE, config_id=0, m=B, n=o.N, k=0, in_buf=(o.x, NONE, NONE), out_buf=o.out,
+                     reserved=(b, o.out2, 0, 0, 0))
+            specs.append((f, [(o.x, b, b + 1, 0, o.N)], [(o.out, b, b + 1, 0, 1), (o.out2, b, b + 1, 0, 1)]))
+        emit_op(specs)
+
+    for o in ops:
+        if o.kind == EMBED:
+            emit_op([(dict(op_id=MEMCPY, config_id=_dtype_code(w.weight_dtype), m=B, n=H, k=0,
+                           in_buf=(o.x, o.w, NONE), out_buf=o.out), [], [(o.out, 0, B, 0, H)])])
+        elif o.kind == MATMUL:
+            gemv_op(o)
+        elif o.kind == NORM:
+            norm_op(o)
+        elif o.kind == ATTN:
+            attention_ops(o)
+        elif o.kind == SAMPLE_OP:
+            sample_op(o)
+        else:
+            raise ValueError(f"unknown op kind {o.kind}")
 
     n = len(rows)
     tasks = np.zeros(n, dtype=TASK_DTYPE)
@@ -301,16 +487,41 @@ def rects_from_descriptor(d, w):
     if op == COMBINE:
         b, h0, hc, _, bs = r
         return [(inb[0], 0, 1, bs, bs + m)], [(out, b, b + 1, h0 * hd, (h0 + hc) * hd)]
+    if op == RMSNORM:
+        b = r[0]
+        reads, writes = [(inb[0], b, b + 1, 0, n)], [(out, b, b + 1, 0, n)]
+        if int(d["flags"]) & FUSED_RESIDUAL:
+            reads.append((inb[2], b, b + 1, 0, n))
+            writes.append((r[1], b, b + 1, 0, n))
+        return reads, writes
+    if op == SAMPLE:
+        b = r[0]
+        return [(inb[0], b, b + 1, 0, n)], [(out, b, b + 1, 0, 1), (r[1], b, b + 1, 0, 1)]
     raise ValueError(f"unexpected op {op}")
 
 
+def external_reads(d, w):
+    """Rows of the per-step inputs tokens and positions a descriptor reads, as (buf,
+    row) pairs: the embedding gather reads every row's token, RoPE-append and the
+    attention partials read their row's position."""
+    op = int(d["op_id"])
+    bi = BufferIndex(w)
+    if op == MEMCPY:
+        return [(bi.tokens, b) for b in range(int(d["m"]))]
+    if op in (APPEND, PARTIAL):
+        return [(bi.positions, int(d["reserved"][0]))]
+    return []
+
+
 def check_graph(tasks, edges, w, brute_ancestors: bool = False):
-    """Invariants I1-I5 (raises AssertionError); returns the parent lists.
+    """Invariants I1-I5 and I7 (raises AssertionError); returns the parent lists.
 
     I1 every edge goes from a lower to a higher index; I2 every earlier writer of an
     overlapping rectangle is an ancestor of the reader; I3 remaining_deps is the
     in-degree and the dependents counts sum to the edge count; I4 no two tasks write
-    overlapping rectangles (single assignment); offsets are the exclusive prefix sum.
+    overlapping rectangles (single assignment); offsets are the exclusive prefix sum;
+    I7 a task that writes a row of tokens or positions (SAMPLE) has every task that
+    reads that row as an ancestor (write after read; needs brute_ancestors).
     """
     n = len(tasks)
     deg = tasks["num_dependents"].astype(np.int64)
@@ -356,6 +567,23 @@ def check_graph(tasks, edges, w, brute_ancestors: bool = False):
                 msk = (a[:, 0] < wrr[2]) & (wrr[1] < a[:, 1]) & (a[:, 2] < wrr[4]) & (wrr[3] < a[:, 3])
                 assert not msk.any(), f"I4: task {t} overwrites buffer {wrr[0]}"
             lst.append((wrr[1], wrr[2], wrr[3], wrr[4], t))
+    bi = BufferIndex(w)
+    ext_readers, ext_writers = {}, {}
+    for t in range(n):
+        for key in external_reads(tasks[t], w):
+            for wt in ext_writers.get(key, []):
+                assert anc is not None, "I7 needs brute_ancestors"
+                assert wt in anc[t], f"I7: task {t} reads {key} after task {wt} wrote it, without an edge"
+            ext_readers.setdefault(key, []).append(t)
+        _, wr = rects_from_descriptor(tasks[t], w)
+        for (buf, r0, r1, _, _) in wr:
+            if buf not in (bi.tokens, bi.positions):
+                continue
+            assert anc is not None, "I7 needs brute_ancestors"
+            for row in range(r0, r1):
+                for rd in ext_readers.get((buf, row), []):
+                    assert rd in anc[t], f"I7: task {t} writes row {row} of buffer {buf} before reader {rd} is done"
+                ext_writers.setdefault((buf, row), []).append(t)
     return par
 
 
@@ -366,5 +594,11 @@ def closed_form_counts(w):
     C = [w.chunks(b) for b in range(B)]
     sumC = sum(C)
     tasks_per_layer = T + B * G + G * sumC + B * G + 3 * T
+    if getattr(w, "unfused", 0):
+        tasks_per_layer += 2 * B       # the attention and MLP norms, one task per row
     n_tasks = 1 + w.n_layers * tasks_per_layer + T
+    if getattr(w, "unfused", 0):
+        n_tasks += B                   # the final norm
+    if getattr(w, "sample", 0):
+        n_tasks += B                   # one SAMPLE per row
     return n_tasks, tasks_per_layer

@@ -17,8 +17,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import decode as od
-from .graph import APPEND, BufferIndex, COMBINE, GEMV, MEMCPY, NOP, PARTIAL, RMS_NORM_INPUT, \
-    SILU_MUL, ADD_RESIDUAL
+from .graph import APPEND, BufferIndex, COMBINE, FUSED_RESIDUAL, GEMV, MEMCPY, NOP, PARTIAL, RMSNORM, \
+    RMS_NORM_INPUT, SAMPLE, SILU_MUL, ADD_RESIDUAL
 
 
 class Stalled(RuntimeError):
@@ -29,6 +29,7 @@ def _act_shapes(w):
     bi = BufferIndex(w)
     B, H, hd = w.batch, w.hidden, w.head_dim
     slots = sum(w.chunks(b) for b in range(B)) * w.n_kv_heads
+    L_ = w.n_layers
     shapes = {bi.x0: (B, H), bi.logits: (B, w.vocab)}
     for l in range(w.n_layers):
         shapes[bi.act(l, 0)] = (B, w.qkv_cols)
@@ -38,14 +39,19 @@ def _act_shapes(w):
         shapes[bi.act(l, 4)] = (B, H)
         shapes[bi.act(l, 5)] = (B, w.intermediate)
         shapes[bi.act(l, 6)] = (B, H)
+        if bi.unfused:
+            for j in range(4):
+                shapes[bi.extra(l, j)] = (B, H)
+    if bi.unfused:
+        shapes[bi.extra(L_, 0)] = (B, H)
     return shapes
 
 
 class Interpreter:
     def __init__(self, w, params, tokens, positions):
         self.w, self.p = w, params
-        self.tokens = np.asarray(tokens)
-        self.positions = np.asarray(positions)
+        self.tokens = np.array(tokens, dtype=np.int64)
+        self.positions = np.array(positions, dtype=np.int64)
         self.buf = {k: np.full(s, np.nan) for k, s in _act_shapes(w).items()}
         self.cache = {}  # (layer, which, b, g) -> float64[pos+1, hd], pre-filled slots
         for l in range(w.n_layers):
@@ -128,6 +134,21 @@ class Interpreter:
             for j in range(hc):
                 parts = [(P[bs + c, j, hd], P[bs + c, j, hd + 1], P[bs + c, j, :hd]) for c in range(m)]
                 self.buf[out][b, (h0 + j) * hd:(h0 + j + 1) * hd] = od.combine(parts)
+            return
+        if op == RMSNORM:
+            b = r[0]
+            v = self.buf[inb[0]][b].copy()
+            if int(d["flags"]) & FUSED_RESIDUAL:
+                v = v + self.buf[inb[2]][b]
+                self.buf[r[1]][b] = v
+            self.buf[out][b] = od.rmsnorm(v, self.p.vector(inb[1]), w.rms_eps)
+            return
+        if op == SAMPLE:
+            # tokens and positions are the step's inputs, updated in place: every task
+            # that reads them must have run already (the edges guarantee it)
+            b = r[0]
+            self.tokens[b] = od.greedy_token(self.buf[inb[0]][b])
+            self.positions[b] += 1
             return
         raise ValueError(f"op {op} not run by this interpreter")
 

@@ -57,6 +57,8 @@ class Workload:
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
     join_nodes: int = 1
+    unfused: int = 0  # 1: lower without the epilogue-fusion pass (standalone RMSNORM tasks)
+    sample: int = 0   # 1: SAMPLE tasks after the lm_head (a whole greedy step per launch)
     seed: int = 0
     meta: dict = field(default_factory=dict, compare=False)
 
@@ -108,7 +110,8 @@ class Workload:
                     vocab=self.vocab, batch=self.batch, rms_eps=self.rms_eps, rope_theta=self.rope_theta,
                     weight_dtype=self.weight_dtype, kv_dtype=self.kv_dtype, gemv_tiles=self.gemv_tiles,
                     kv_chunk=self.kv_chunk, join_nodes=self.join_nodes, gemv_config=self.gemv_config,
-                    kv_capacity=self.kv_capacity, kv_len=self.kv_len)
+                    kv_capacity=self.kv_capacity, kv_len=self.kv_len,
+                    options=(1 if self.unfused else 0) | (2 if self.sample else 0))
 
     # ---- per-step inputs ----------------------------------------------
     def tokens(self) -> np.ndarray:

@@ -26,6 +26,8 @@ MK_STATIC_SCRATCH_BYTES = 64 << 20
 (MK_OP_NOP, MK_OP_MEMCPY, MK_OP_GEMV, MK_OP_RMSNORM, MK_OP_ATTENTION, MK_OP_MLP, MK_OP_SAMPLE,
  MK_OP_ATTENTION_APPEND, MK_OP_ATTENTION_PARTIAL, MK_OP_ATTENTION_COMBINE) = range(10)
 MK_FLAG_SILU_MUL, MK_FLAG_ADD_RESIDUAL, MK_FLAG_RMS_NORM_INPUT = 1, 2, 4
+MK_FLAG_FUSED_RESIDUAL = 2
+MK_LOWER_UNFUSED, MK_LOWER_SAMPLE = 1, 2
 # numpy mirror of mk_task_t (64 bytes), for reading the descriptor array on the host.
 MK_TASK_DTYPE = np.dtype({
     "names": ["op_id", "config_id", "step", "flags", "remaining_deps", "num_dependents", "dependents_offset",
@@ -60,7 +62,7 @@ class MkModelCfg(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("batch", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("gemv_tiles", ctypes.c_int32), ("kv_chunk", ctypes.c_int32), ("join_nodes", ctypes.c_int32),
-                ("gemv_config", ctypes.c_int32), ("kv_capacity", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("gemv_config", ctypes.c_int32), ("kv_capacity", ctypes.c_int32), ("options", ctypes.c_int32),
                 ("kv_len", ctypes.POINTER(ctypes.c_int32))]
 
 
@@ -147,12 +149,12 @@ def mk_abi_version() -> int:
 
 def make_cfg(*, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, batch, rms_eps,
              rope_theta, weight_dtype, kv_dtype, gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity,
-             kv_len):
+             kv_len, options=0):
     """Build an mk_model_cfg; returns (cfg, keepalive) -- keep both alive during calls."""
     kv = (ctypes.c_int32 * batch)(*[int(v) for v in kv_len])
     c = MkModelCfg(MK_ABI_VERSION, ctypes.sizeof(MkModelCfg), n_layers, hidden, n_q_heads, n_kv_heads, head_dim,
                    intermediate, vocab, batch, rms_eps, rope_theta, MK_DTYPE[weight_dtype], MK_DTYPE[kv_dtype],
-                   gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity, 0,
+                   gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity, options,
                    ctypes.cast(kv, ctypes.POINTER(ctypes.c_int32)))
     return c, kv
 

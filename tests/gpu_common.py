@@ -135,6 +135,11 @@ class MkRun:
                 else:
                     a = a.reshape(w.batch, -1)
                 out[f"l{l}.{nm}"] = a
+            if bi.unfused:
+                for j, nm in enumerate(["xn", "o", "hn", "d"]):
+                    out[f"l{l}.{nm}"] = self.activation(bi.extra(l, j)).reshape(w.batch, -1)
+        if bi.unfused:
+            out["xn_final"] = self.activation(bi.extra(w.n_layers, 0)).reshape(w.batch, -1)
         return out
 
     def close(self):
@@ -161,7 +166,12 @@ def compare_activations(w, gpu: dict, ref: dict, rows, tol=None):
     def note(kind, e):
         worst[kind] = max(worst.get(kind, 0.0), e)
 
+    standard = {"x0"} | {f"l{l}.{nm}" for l in range(w.n_layers)
+                         for nm in ("qkv_out", "q_rot", "partials", "att", "h", "gu", "x_out")}
+    assert standard <= set(gpu), "the GPU step is missing an activation buffer"
     for name, rv in ref.items():
+        if name not in gpu:  # buffers of the unfused graph only
+            continue
         kind = name.split(".")[-1]
         if name.endswith("partials"):
             gv = gpu[name]
