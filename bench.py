@@ -184,16 +184,17 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str
 
 def greedy_run(w, inp, n_tokens, stream):
     """Greedy decode of n_tokens tokens from the timed step's position onward, with a
-    graph lowered for n_tokens more cache slots on the same weights.  The loop never
-    touches the host: mk_decode_greedy enqueues every step followed by the library's
-    SAMPLE kernel (argmax, lowest index on ties, and the position update).  Returns
-    time between tokens."""
+    graph lowered for n_tokens more cache slots on the same weights, with SAMPLE tasks
+    at its end.  The loop never touches the host: mk_decode_greedy enqueues one launch
+    per token, whose SAMPLE tasks pick the tokens (argmax, lowest index on ties) and
+    advance the positions.  Returns time between tokens."""
     import torch
 
     import task_graph_interpreter_amd as mk
     from synth.device import DeviceInputs
 
-    w2 = w.replace(kv_len=tuple(int(l) + n_tokens for l in w.kv_len), kv_capacity=w.kv_capacity + n_tokens)
+    w2 = w.replace(kv_len=tuple(int(l) + n_tokens for l in w.kv_len), kv_capacity=w.kv_capacity + n_tokens,
+                   sample=1)
     inp2 = DeviceInputs(w2, weights=inp.weights)
     cfg2, keep2 = mk.make_cfg(**w2.mk_fields())
     plan2 = mk.mk_plan(cfg2)
@@ -216,8 +217,8 @@ def greedy_run(w, inp, n_tokens, stream):
     log(f"greedy: {n_tokens} tokens, {total / n_tokens:.4f} ms between tokens")
     return {"tokens": n_tokens, "ms_per_token": total / n_tokens, "tokens_per_s": w.batch * n_tokens / (total / 1e3),
             "first_position": int(w.positions()[0]), "kv_slots": w2.kv_capacity,
-            "note": "graph lowered for kv_len + tokens (empty chunks until reached); mk_decode_greedy: "
-                    "each step followed by the SAMPLE kernel (argmax and position update), no host round trip"}
+            "note": "graph lowered for kv_len + tokens (empty chunks until reached) with SAMPLE tasks after the "
+                    "lm_head; mk_decode_greedy: one launch per token, no host round trip"}
 
 
 def timed(fn, steps, warmup, stream, ptrs):

@@ -65,6 +65,13 @@ extern "C" {
  *                first partial slot of (b, g)}; in_buf = {q_rot, kcache, vcache}
  *   ATTENTION_COMBINE (9): as PARTIAL with reserved[3] = 0; in_buf = {partials}
  *   MEMCPY (1):  embedding gather, m = batch, n = hidden; in_buf = {tokens, E}
+ *   RMSNORM (3): row b = reserved[0] of out = rmsnorm(x [+ residual]) * gamma; m =
+ *                batch, n = hidden; in_buf = {x, gamma, residual | none}; flags
+ *                FUSED_RESIDUAL: the sum x + residual is also written to buffer
+ *                reserved[1]
+ *   SAMPLE (6):  row b = reserved[0]: out (the tokens buffer)[b] = argmax of row b of
+ *                in_buf[0] (the logits; lowest index on ties), positions (buffer
+ *                reserved[1])[b] += 1; m = batch, n = vocab
  *   NOP (0):     join node; only the dependency fields are set.
  * remaining_deps is the in-degree (constant; run-time readiness uses separate
  * counters).  step is always 0.  config_id selects the body variant: GEMV 0 fp32,
@@ -94,6 +101,7 @@ enum {
   MK_OP_ATTENTION_COMBINE = 9
 };
 enum { MK_FLAG_SILU_MUL = 1, MK_FLAG_ADD_RESIDUAL = 2, MK_FLAG_RMS_NORM_INPUT = 4 };
+enum { MK_FLAG_FUSED_RESIDUAL = 2 }; /* the same bit on an RMSNORM descriptor */
 
 enum { MK_DTYPE_F32 = 0, MK_DTYPE_BF16 = 1 };
 enum { MK_GEMV_F32 = 0, MK_GEMV_BF16 = 1, MK_GEMV_BF16_MFMA = 2 };
@@ -118,9 +126,28 @@ typedef struct mk_model_cfg {
   int32_t join_nodes;             /* 1: insert NOP join tasks for shared parent sets */
   int32_t gemv_config;            /* MK_GEMV_* */
   int32_t kv_capacity;            /* cache slots per (layer, sequence, KV head) */
-  int32_t reserved0;
+  int32_t options;                /* MK_LOWER_* bits (0: fused step, logits only) */
   const int32_t* kv_len;          /* host pointer, [batch] */
 } mk_model_cfg;
+
+/* Lowering options ("Mega kernel initial": the graph-API section writes the decoder
+ * with its fusions given by hand and names a pass that finds them automatically as
+ * future work; the OpId table lists RMSNORM and SAMPLE).  The lowering first writes
+ * the step as a list of ops with no fusion -- every RMSNorm its own op, each residual
+ * add carried by the next RMSNorm (FUSED_RESIDUAL) -- then runs that pass, which
+ * folds each residual add into the matmul producing the summand (ADD_RESIDUAL) and
+ * each RMSNorm read only by matmuls into them (RMS_NORM_INPUT); the result is the
+ * hand-fused decoder.
+ *   MK_LOWER_UNFUSED: skip the pass.  Every RMSNorm runs as RMSNORM tasks (one per
+ *     batch row) and the graph has 4 n_layers + 1 more activation buffers (BufIdx
+ *     order: after the logits, per layer the normed attention input, the o-projection
+ *     output, the normed MLP input, the down-projection output; then the normed
+ *     lm_head input).
+ *   MK_LOWER_SAMPLE: one SAMPLE task per batch row after the lm_head, so a step
+ *     writes each row's greedy token (argmax, lowest index on ties) into tokens_dev
+ *     and advances positions_dev: one launch runs a whole greedy step. */
+#define MK_LOWER_UNFUSED 1
+#define MK_LOWER_SAMPLE 2
 
 /* Weights in canonical order (buffer-table section of the page: append-only, one
  * index per tensor): [0] embedding [vocab, hidden]; per layer l at 1 + 6 l:
@@ -232,9 +259,11 @@ int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
 int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t* tokens_dev,
                      int32_t* positions_dev);
 
-/* n_steps greedy decode steps with no host round trip: each is mk_decode_step on these
- * buffers followed by mk_sample_greedy, so step i + 1 embeds step i's tokens at the
- * next positions and appends to the same caches.  When tokens_out_dev is non-NULL
+/* n_steps greedy decode steps with no host round trip, so step i + 1 embeds step i's
+ * tokens at the next positions and appends to the same caches.  For a graph built with
+ * MK_LOWER_SAMPLE each step is ONE launch (its SAMPLE tasks pick the tokens and advance
+ * the positions); otherwise each step is mk_decode_step on these buffers followed by
+ * mk_sample_greedy.  When tokens_out_dev is non-NULL
  * (device, n_steps * batch int32), step i's tokens are also written to
  * tokens_out_dev[i * batch + b].  Positions must stay below each sequence's kv_len
  * (the graph's chunk fan-out); a step past it sets MK_STATUS_BAD_POSITION, which

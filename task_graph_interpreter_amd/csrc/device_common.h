@@ -69,6 +69,7 @@ struct LaunchArgs {
   uint32_t* arrivals;  // one counter per kArrivalStride words
   Ctrl* ctrl;
   uint64_t* trace;
+  int32_t* tokens_out;  // SAMPLE tasks also write their token here when non-null ([batch])
   uint64_t rt[8];  // per-step bases indexed by tag
   uint32_t n_tasks;
   uint32_t epoch;

@@ -14,6 +14,7 @@ namespace mk {
 // caches, then the step's activations in emission order, then logits).
 struct BufIdx {
   int L = 0;
+  bool unfused = false;  // five more activation buffers per layer group (extra())
   uint32_t tokens() const { return 0; }
   uint32_t positions() const { return 1; }
   uint32_t embedding() const { return 2; }
@@ -24,8 +25,13 @@ struct BufIdx {
   // which: 0 qkv_out, 1 q_rot, 2 partials, 3 att, 4 h, 5 gu, 6 x_out
   uint32_t act(int l, int which) const { return 6u + 8u * L + 7u * l + which; }
   uint32_t logits() const { return 6u + 15u * L; }
-  uint32_t count() const { return 7u + 15u * L; }
+  // Graphs lowered without epilogue fusion only, appended after the logits.  which:
+  // 0 normed attention input, 1 o-projection output, 2 normed MLP input, 3 down-
+  // projection output; l = L with which 0: the normed input of the lm_head.
+  uint32_t extra(int l, int which) const { return 7u + 15u * L + 4u * l + which; }
+  uint32_t count() const { return 7u + 15u * L + (unfused ? 4u * L + 1u : 0u); }
 };
+
 
 enum { W_ATTN_NORM = 0, W_QKV, W_O, W_MLP_NORM, W_GATE_UP, W_DOWN, KCACHE, VCACHE };
 constexpr uint16_t kNone = 0xFFFF;

@@ -105,6 +105,8 @@ __device__ __forceinline__ bool run_task_spec(const LaunchArgs& a, const mk_task
     case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16, S::BM == 32>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
     case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
+    case MK_OP_RMSNORM: task_rmsnorm(a, d, t, sm); break;
+    case MK_OP_SAMPLE: task_sample(a, d, t, sm); break;
     default: break;  // NOP joins never run as tasks: their children poll their counter
   }
   return ahead;

@@ -17,7 +17,15 @@
 //    rotates the group's q heads and its k head and appends k and v;
 //  * join NOPs: for an op with >= 2 tasks whose tasks share >= 2 parents, one NOP with
 //    those parents is emitted just before the op and replaces them in every task's
-//    parent list (a T x T boundary becomes 2 T edges).
+//    parent list (a T x T boundary becomes 2 T edges);
+//  * the step is first written as a list of ops the way the page's graph API builds it,
+//    with no fusion: every RMSNorm its own op, each residual add carried by the next
+//    RMSNorm (FUSED_RESIDUAL, flags paragraph).  The epilogue-fusion pass the graph-API
+//    section names as future work then folds each residual add into the matmul that
+//    produced the summand and each RMSNorm read only by matmuls into those matmuls,
+//    which gives the hand-fused decoder of that section; MK_LOWER_UNFUSED skips it.
+//    RMSNORM (OpId 3) is one task per batch row; with MK_LOWER_SAMPLE one SAMPLE task
+//    (OpId 6) per row follows the lm_head.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
@@ -43,8 +51,8 @@ struct PendingTask {
   mk_task_t d;
   Rect reads[3];
   int n_reads;
-  Rect write;
-  bool has_write;
+  Rect writes[2];
+  int n_writes;
 };
 
 inline bool overlap(const Writer& w, const Rect& r) {
@@ -102,8 +110,8 @@ class Builder {
       uint32_t idx = (uint32_t)L_.tasks.size();
       L_.tasks.push_back(op[i].d);
       parents_.push_back(std::move(par[i]));
-      if (op[i].has_write) {
-        const Rect& w = op[i].write;
+      for (int k = 0; k < op[i].n_writes; ++k) {
+        const Rect& w = op[i].writes[k];
         writers_[w.buf].push_back(Writer{w.r0, w.r1, w.c0, w.c1, idx});
       }
     }
@@ -145,6 +153,132 @@ class Builder {
   std::vector<std::vector<Writer>> writers_;
   std::vector<std::vector<uint32_t>> parents_;
 };
+
+// One op of the step before its fan-out into tasks.  MATMUL: out = x W^T with the
+// epilogue flags gamma (RMS_NORM_INPUT), residual (ADD_RESIDUAL) and silu (SILU_MUL).
+// NORM: out = rmsnorm(x [+ residual]) * gamma, also writing the sum to out2 when there
+// is a residual (FUSED_RESIDUAL).  ATTN: layer `layer` from its qkv input x.  EMBED:
+// x0 from the tokens.  SAMPLE: greedy token of each row of x into out (tokens), the
+// row's position (out2) advanced.
+enum class OpKind { EMBED, NORM, MATMUL, ATTN, SAMPLE };
+
+struct Op {
+  OpKind kind;
+  uint32_t out, x = kNone, w = kNone, gamma = kNone, residual = kNone, out2 = kNone;
+  bool silu = false;
+  int64_t K = 0, N = 0;
+  int layer = -1;
+  bool dead = false;
+};
+
+// The decode step written with the graph API and no fusion.
+std::vector<Op> decoder_program(const mk_model_cfg& c, const BufIdx& bi) {
+  const int64_t H = c.hidden, I = c.intermediate, V = c.vocab, L = c.n_layers;
+  const int64_t qkv_cols = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim,
+                qcols = (int64_t)c.n_q_heads * c.head_dim;
+  std::vector<Op> ops;
+  auto add = [&](Op o) { ops.push_back(o); };
+  {
+    Op e{OpKind::EMBED, bi.x0()};
+    e.x = bi.tokens();
+    e.w = bi.embedding();
+    add(e);
+  }
+  uint32_t x_in = bi.x0();
+  for (int l = 0; l < L; ++l) {
+    Op n1{OpKind::NORM, bi.extra(l, 0)};
+    n1.gamma = bi.layer(l, W_ATTN_NORM);
+    n1.N = H;
+    if (l == 0) {
+      n1.x = bi.x0();
+    } else {  // the previous layer's residual add rides on this norm
+      n1.x = bi.extra(l - 1, 3);
+      n1.residual = bi.act(l - 1, 4);
+      n1.out2 = x_in;
+    }
+    add(n1);
+    Op q{OpKind::MATMUL, bi.act(l, 0)};
+    q.x = bi.extra(l, 0), q.w = bi.layer(l, W_QKV), q.K = H, q.N = qkv_cols;
+    add(q);
+    Op a{OpKind::ATTN, bi.act(l, 3)};
+    a.x = bi.act(l, 0), a.layer = l;
+    add(a);
+    Op o{OpKind::MATMUL, bi.extra(l, 1)};
+    o.x = bi.act(l, 3), o.w = bi.layer(l, W_O), o.K = qcols, o.N = H;
+    add(o);
+    Op n2{OpKind::NORM, bi.extra(l, 2)};
+    n2.x = bi.extra(l, 1), n2.gamma = bi.layer(l, W_MLP_NORM), n2.residual = x_in, n2.out2 = bi.act(l, 4), n2.N = H;
+    add(n2);
+    Op g{OpKind::MATMUL, bi.act(l, 5)};
+    g.x = bi.extra(l, 2), g.w = bi.layer(l, W_GATE_UP), g.silu = true, g.K = H, g.N = I;
+    add(g);
+    Op d{OpKind::MATMUL, bi.extra(l, 3)};
+    d.x = bi.act(l, 5), d.w = bi.layer(l, W_DOWN), d.K = I, d.N = H;
+    add(d);
+    x_in = bi.act(l, 6);
+  }
+  Op nf{OpKind::NORM, bi.extra((int)L, 0)};
+  nf.x = bi.extra((int)L - 1, 3), nf.gamma = bi.final_norm(), nf.residual = bi.act((int)L - 1, 4), nf.out2 = x_in;
+  nf.N = H;
+  add(nf);
+  Op lm{OpKind::MATMUL, bi.logits()};
+  lm.x = bi.extra((int)L, 0), lm.w = bi.w_lm(), lm.K = H, lm.N = V;
+  add(lm);
+  return ops;
+}
+
+// The automatic epilogue-fusion pass.
+//  1. A norm with a residual whose input is written by a matmul with no epilogue and
+//     read by nothing else: the matmul adds the residual itself (ADD_RESIDUAL) and
+//     writes the sum; the norm then reads the sum with no residual.
+//  2. A norm with no residual whose every reader is a matmul taking it as its input,
+//     with neither an input norm nor a residual (one gamma/residual slot per
+//     descriptor): each reader reads the norm's input with RMS_NORM_INPUT, and the
+//     norm is dropped.
+void fuse_epilogues(std::vector<Op>& ops) {
+  auto readers = [&](uint32_t buf) {
+    std::vector<size_t> r;
+    for (size_t i = 0; i < ops.size(); ++i)
+      if (!ops[i].dead && (ops[i].x == buf || ops[i].residual == buf)) r.push_back(i);
+    return r;
+  };
+  auto writers = [&](uint32_t buf) {
+    std::vector<size_t> r;
+    for (size_t i = 0; i < ops.size(); ++i)
+      if (!ops[i].dead && (ops[i].out == buf || ops[i].out2 == buf)) r.push_back(i);
+    return r;
+  };
+  for (size_t i = 0; i < ops.size(); ++i) {
+    Op& n = ops[i];
+    if (n.kind != OpKind::NORM || n.residual == kNone) continue;
+    const std::vector<size_t> wr = writers(n.x), rd = readers(n.x);
+    if (wr.size() != 1 || rd.size() != 1 || rd[0] != i) continue;
+    Op& m = ops[wr[0]];
+    if (m.kind != OpKind::MATMUL || m.gamma != kNone || m.residual != kNone || m.silu) continue;
+    m.residual = n.residual;
+    m.out = n.out2;
+    n.x = n.out2;
+    n.residual = kNone;
+    n.out2 = kNone;
+  }
+  for (size_t i = 0; i < ops.size(); ++i) {
+    Op& n = ops[i];
+    if (n.dead || n.kind != OpKind::NORM || n.residual != kNone) continue;
+    const std::vector<size_t> rd = readers(n.out);
+    bool ok = !rd.empty();
+    for (size_t r : rd) {
+      const Op& m = ops[r];
+      ok = ok && m.kind == OpKind::MATMUL && m.x == n.out && m.gamma == kNone && m.residual == kNone;
+    }
+    if (!ok) continue;
+    for (size_t r : rd) {
+      ops[r].x = n.x;
+      ops[r].gamma = n.gamma;
+    }
+    n.dead = true;
+  }
+  ops.erase(std::remove_if(ops.begin(), ops.end(), [](const Op& o) { return o.dead; }), ops.end());
+}
 
 void tile_range(int64_t N, int64_t T, int64_t i, bool mfma, int64_t& c0, int64_t& c1) {
   if (mfma) {
@@ -191,7 +325,9 @@ int validate_cfg(const mk_model_cfg* c) {
       return set_error(MK_ERR_INVALID, "gemv_tiles must be in [1, N] for every matmul");
     }
   }
-  if (7ll + 15ll * c->n_layers > 0xFFFF) return set_error(MK_ERR_INVALID, "more than 65535 buffers");
+  if (c->options & ~(MK_LOWER_UNFUSED | MK_LOWER_SAMPLE)) return set_error(MK_ERR_INVALID, "unknown bit in options");
+  if (7ll + 15ll * c->n_layers + ((c->options & MK_LOWER_UNFUSED) ? 4ll * c->n_layers + 1 : 0) > 0xFFFF)
+    return set_error(MK_ERR_INVALID, "more than 65535 buffers");
   // Limits of the device task bodies: GEMV rows are streamed in 16-byte pieces and an
   // input row is staged in the 148 KB LDS area; a KV row is read by a power-of-two
   // group of lanes, 16 bytes each.  The chunk length and the number of chunks have no
@@ -232,6 +368,7 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
   L.kv_len.assign(cfg->kv_len, cfg->kv_len + cfg->batch);
   L.cfg.kv_len = L.kv_len.data();
   L.bi.L = cfg->n_layers;
+  L.bi.unfused = (cfg->options & MK_LOWER_UNFUSED) != 0;
   const BufIdx& bi = L.bi;
 
   const int64_t B = cfg->batch, H = cfg->hidden, hd = cfg->head_dim, Hq = cfg->n_q_heads,
@@ -271,68 +408,138 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
     place(bi.act(l, 5), 4ull * B * I);
     place(bi.act(l, 6), 4ull * B * H);
   }
+  if (bi.unfused) {
+    for (int l = 0; l < cfg->n_layers; ++l)
+      for (int j = 0; j < 4; ++j) place(bi.extra(l, j), 4ull * B * H);
+    place(bi.extra(cfg->n_layers, 0), 4ull * B * H);
+  }
   L.scratch_total = off;
   L.kv_layer_bytes = (uint64_t)B * Hkv * cfg->kv_capacity * hd * (cfg->kv_dtype == MK_DTYPE_F32 ? 4 : 2);
+
+  std::vector<Op> ops = decoder_program(*cfg, bi);
+  if (!bi.unfused) fuse_epilogues(ops);
+  if (cfg->options & MK_LOWER_SAMPLE) {
+    Op smp{OpKind::SAMPLE, bi.tokens()};
+    smp.x = bi.logits();
+    smp.out2 = bi.positions();
+    smp.N = V;
+    ops.push_back(smp);
+  }
 
   Builder bld(L);
   std::vector<PendingTask> op;
 
-  auto gemv = [&](uint32_t x, int64_t K, uint32_t W, int64_t N, uint16_t flags, uint32_t aux, uint32_t y) {
+  auto gemv = [&](const Op& o) {
+    const uint16_t flags = (uint16_t)((o.gamma != kNone ? MK_FLAG_RMS_NORM_INPUT : 0) |
+                                      (o.residual != kNone ? MK_FLAG_ADD_RESIDUAL : 0) | (o.silu ? MK_FLAG_SILU_MUL : 0));
+    const uint32_t aux = o.gamma != kNone ? o.gamma : o.residual;
     op.clear();
     for (int64_t i = 0; i < T; ++i) {
       int64_t c0, c1;
-      tile_range(N, T, i, mfma, c0, c1);
+      tile_range(o.N, T, i, mfma, c0, c1);
       PendingTask p{};
       p.d = blank();
       p.d.op_id = MK_OP_GEMV;
       p.d.config_id = (uint16_t)cfg->gemv_config;
       p.d.flags = flags;
       p.d.m = (int32_t)B;
-      p.d.n = (int32_t)N;
-      p.d.k = (int32_t)K;
-      p.d.in_buf[0] = (uint16_t)x;
-      p.d.in_buf[1] = (uint16_t)W;
+      p.d.n = (int32_t)o.N;
+      p.d.k = (int32_t)o.K;
+      p.d.in_buf[0] = (uint16_t)o.x;
+      p.d.in_buf[1] = (uint16_t)o.w;
       p.d.in_buf[2] = (uint16_t)aux;
-      p.d.out_buf = (uint16_t)y;
+      p.d.out_buf = (uint16_t)o.out;
       p.d.reserved[0] = (uint32_t)c0;
       p.d.reserved[1] = (uint32_t)(c1 - c0);
-      p.d.reserved[2] = (flags & MK_FLAG_SILU_MUL) ? (uint32_t)I : 0u;
-      p.reads[0] = Rect{x, 0, B, 0, K};
+      p.d.reserved[2] = o.silu ? (uint32_t)I : 0u;
+      p.reads[0] = Rect{o.x, 0, B, 0, o.K};
       p.n_reads = 1;
-      if (flags & MK_FLAG_ADD_RESIDUAL) p.reads[p.n_reads++] = Rect{aux, 0, B, c0, c1};
-      p.write = Rect{y, 0, B, c0, c1};
-      p.has_write = true;
+      if (o.residual != kNone) p.reads[p.n_reads++] = Rect{o.residual, 0, B, c0, c1};
+      p.writes[0] = Rect{o.out, 0, B, c0, c1};
+      p.n_writes = 1;
       op.push_back(p);
     }
     bld.emit(op);
   };
 
-  // Embedding gather.
-  op.clear();
-  {
+  // One task per batch row: the norm needs the whole row.
+  auto norm = [&](const Op& o) {
+    op.clear();
+    for (int64_t b = 0; b < B; ++b) {
+      PendingTask p{};
+      p.d = blank();
+      p.d.op_id = MK_OP_RMSNORM;
+      p.d.config_id = (uint16_t)cfg->weight_dtype;
+      p.d.flags = o.residual != kNone ? (uint16_t)MK_FLAG_FUSED_RESIDUAL : (uint16_t)0;
+      p.d.m = (int32_t)B;
+      p.d.n = (int32_t)o.N;
+      p.d.in_buf[0] = (uint16_t)o.x;
+      p.d.in_buf[1] = (uint16_t)o.gamma;
+      p.d.in_buf[2] = (uint16_t)o.residual;
+      p.d.out_buf = (uint16_t)o.out;
+      p.d.reserved[0] = (uint32_t)b;
+      p.d.reserved[1] = o.out2;
+      p.reads[0] = Rect{o.x, b, b + 1, 0, o.N};
+      p.n_reads = 1;
+      p.writes[0] = Rect{o.out, b, b + 1, 0, o.N};
+      p.n_writes = 1;
+      if (o.residual != kNone) {
+        p.reads[p.n_reads++] = Rect{o.residual, b, b + 1, 0, o.N};
+        p.writes[p.n_writes++] = Rect{o.out2, b, b + 1, 0, o.N};
+      }
+      op.push_back(p);
+    }
+    bld.emit(op);
+  };
+
+  // One task per batch row after the lm_head: writes the row's greedy token and
+  // advances its position.
+  auto sample = [&](const Op& o) {
+    op.clear();
+    for (int64_t b = 0; b < B; ++b) {
+      PendingTask p{};
+      p.d = blank();
+      p.d.op_id = MK_OP_SAMPLE;
+      p.d.m = (int32_t)B;
+      p.d.n = (int32_t)o.N;
+      p.d.in_buf[0] = (uint16_t)o.x;
+      p.d.out_buf = (uint16_t)o.out;
+      p.d.reserved[0] = (uint32_t)b;
+      p.d.reserved[1] = o.out2;
+      p.reads[0] = Rect{o.x, b, b + 1, 0, o.N};
+      p.n_reads = 1;
+      p.writes[0] = Rect{o.out, b, b + 1, 0, 1};
+      p.writes[1] = Rect{o.out2, b, b + 1, 0, 1};
+      p.n_writes = 2;
+      op.push_back(p);
+    }
+    bld.emit(op);
+  };
+
+  auto embed = [&](const Op& o) {
+    op.clear();
     PendingTask p{};
     p.d = blank();
     p.d.op_id = MK_OP_MEMCPY;
     p.d.config_id = (uint16_t)cfg->weight_dtype;
     p.d.m = (int32_t)B;
     p.d.n = (int32_t)H;
-    p.d.in_buf[0] = (uint16_t)bi.tokens();
-    p.d.in_buf[1] = (uint16_t)bi.embedding();
-    p.d.out_buf = (uint16_t)bi.x0();
+    p.d.in_buf[0] = (uint16_t)o.x;
+    p.d.in_buf[1] = (uint16_t)o.w;
+    p.d.out_buf = (uint16_t)o.out;
     p.n_reads = 0;
-    p.write = Rect{bi.x0(), 0, B, 0, H};
-    p.has_write = true;
+    p.writes[0] = Rect{o.out, 0, B, 0, H};
+    p.n_writes = 1;
     op.push_back(p);
     bld.emit(op);
-  }
+  };
 
-  uint32_t x = bi.x0();
-  for (int l = 0; l < cfg->n_layers; ++l) {
-    const uint32_t qkv = bi.act(l, 0), qrot = bi.act(l, 1), part = bi.act(l, 2), att = bi.act(l, 3),
-                   hb = bi.act(l, 4), gu = bi.act(l, 5), xo = bi.act(l, 6);
+  // RoPE-append per (sequence, KV head), a partial per (sequence, KV head, chunk), a
+  // combine per (sequence, KV head).
+  auto attention = [&](const Op& ao) {
+    const int l = ao.layer;
+    const uint32_t qkv = ao.x, qrot = bi.act(l, 1), part = bi.act(l, 2), att = ao.out;
     const uint32_t kc = bi.layer(l, KCACHE), vc = bi.layer(l, VCACHE);
-    gemv(x, H, bi.layer(l, W_QKV), qkv_cols, MK_FLAG_RMS_NORM_INPUT, bi.layer(l, W_ATTN_NORM), qkv);
-
     op.clear();
     for (int64_t b = 0; b < B; ++b)
       for (int64_t g = 0; g < Hkv; ++g) {
@@ -356,8 +563,8 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
         p.reads[1] = Rect{qkv, b, b + 1, k0, k0 + hd};
         p.reads[2] = Rect{qkv, b, b + 1, v0, v0 + hd};
         p.n_reads = 3;
-        p.write = Rect{qrot, b, b + 1, q0, q0 + grp * hd};
-        p.has_write = true;
+        p.writes[0] = Rect{qrot, b, b + 1, q0, q0 + grp * hd};
+        p.n_writes = 1;
         op.push_back(p);
       }
     bld.emit(op);
@@ -387,8 +594,8 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
           const int64_t q0 = g * grp * hd;
           p.reads[0] = Rect{qrot, b, b + 1, q0, q0 + grp * hd};
           p.n_reads = 1;
-          p.write = Rect{part, 0, 1, sb + c, sb + c + 1};
-          p.has_write = true;
+          p.writes[0] = Rect{part, 0, 1, sb + c, sb + c + 1};
+          p.n_writes = 1;
           op.push_back(p);
         }
     bld.emit(op);
@@ -413,18 +620,22 @@ int lower(const mk_model_cfg* cfg, Lowered& L) {
         const int64_t q0 = g * grp * hd;
         p.reads[0] = Rect{part, 0, 1, sb, sb + chunks[b]};
         p.n_reads = 1;
-        p.write = Rect{att, b, b + 1, q0, q0 + grp * hd};
-        p.has_write = true;
+        p.writes[0] = Rect{att, b, b + 1, q0, q0 + grp * hd};
+        p.n_writes = 1;
         op.push_back(p);
       }
     bld.emit(op);
+  };
 
-    gemv(att, qcols, bi.layer(l, W_O), H, MK_FLAG_ADD_RESIDUAL, x, hb);
-    gemv(hb, H, bi.layer(l, W_GATE_UP), I, MK_FLAG_RMS_NORM_INPUT | MK_FLAG_SILU_MUL, bi.layer(l, W_MLP_NORM), gu);
-    gemv(gu, I, bi.layer(l, W_DOWN), H, MK_FLAG_ADD_RESIDUAL, hb, xo);
-    x = xo;
+  for (const Op& o : ops) {
+    switch (o.kind) {
+      case OpKind::EMBED: embed(o); break;
+      case OpKind::NORM: norm(o); break;
+      case OpKind::MATMUL: gemv(o); break;
+      case OpKind::ATTN: attention(o); break;
+      case OpKind::SAMPLE: sample(o); break;
+    }
   }
-  gemv(x, H, bi.w_lm(), V, MK_FLAG_RMS_NORM_INPUT, bi.final_norm(), bi.logits());
   bld.finish();
   // A NOP join never runs: its children poll its counter in place of its own
   // arrival, which only works one level deep, so a NOP must never feed another NOP.

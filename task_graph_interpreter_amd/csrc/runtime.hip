@@ -593,6 +593,17 @@ int mk_decode_greedy(mk_graph* g, void* stream, int n_steps, int32_t* tokens_dev
   if (misaligned(tokens_out_dev, 4)) return mk::set_error(MK_ERR_ALIGN, "tokens_out must be 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const int batch = g->low.cfg.batch;
+  if (g->low.cfg.options & MK_LOWER_SAMPLE) {
+    // SAMPLE tasks end the graph: one launch per token.
+    int rc = check_step_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+    if (rc || (rc = check_workspace(g))) return rc;
+    for (int i = 0; i < n_steps; ++i) {
+      mk::LaunchArgs a = make_args(g, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
+      a.tokens_out = tokens_out_dev ? tokens_out_dev + (size_t)i * batch : nullptr;
+      if ((rc = launch_step(g, s, a)) != MK_OK) return rc;
+    }
+    return MK_OK;
+  }
   for (int i = 0; i < n_steps; ++i) {
     int rc = mk_decode_step(g, stream, tokens_dev, positions_dev, kcache_dev, vcache_dev, logits_dev);
     if (rc) return rc;

@@ -88,6 +88,42 @@ def test_cpp_lowering_equals_oracle_lowering(name, joins):
     assert plan["n_levels"] == int(og.levels(tasks, edges).max()) + 1
 
 
+@pytest.mark.parametrize("opts", [dict(unfused=1), dict(sample=1), dict(unfused=1, sample=1)])
+@pytest.mark.parametrize("name", ["tiny", "1b_b1", "8b_b8_ragged"])
+@pytest.mark.parametrize("joins", [1, 0])
+def test_cpp_lowering_options_equal_oracle_lowering(name, joins, opts):
+    # The unfused graph (standalone RMSNORM tasks) and the SAMPLE tasks, lowered by
+    # both builders.
+    w = workloads.get(name).replace(join_nodes=joins, **opts)
+    cfg, keep = _cfg(w)
+    lo = mk.mk_lower(cfg)
+    tasks, edges = og.build_graph(w)
+    assert np.array_equal(lo.tasks_bytes(), tasks.view(np.uint8).reshape(-1, 64))
+    assert np.array_equal(lo.edges(), edges)
+    plan = mk.mk_plan(cfg)
+    assert plan["n_buffers"] == og.BufferIndex(w).count
+
+
+def test_unfused_scratch_holds_the_extra_buffers():
+    w = workloads.tiny().replace(batch=3, kv_len=(128, 41, 97), unfused=1)
+    cfg, keep = _cfg(w)
+    lo = mk.mk_lower(cfg)
+    bi = og.BufferIndex(w)
+    fused = mk.mk_plan(_cfg(w.replace(unfused=0))[0])["scratch_bytes"]
+    extras = [bi.extra(l, j) for l in range(w.n_layers) for j in range(4)] + [bi.extra(w.n_layers, 0)]
+    spans = [lo.scratch_span(b) for b in extras]
+    assert all(nb == 4 * w.batch * w.hidden for _, nb in spans)
+    assert min(o for o, _ in spans) >= fused  # appended after the fused graph's buffers
+    assert mk.mk_plan(cfg)["scratch_bytes"] >= spans[-1][0] + spans[-1][1]
+
+
+def test_unknown_option_rejected():
+    cfg, keep = _cfg(workloads.tiny(), options=8)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan(cfg)
+    assert e.value.code == binding.MK_ERR_INVALID and "options" in str(e.value)
+
+
 def test_scratch_layout():
     w = workloads.llama8b_ragged()
     cfg, keep = _cfg(w)

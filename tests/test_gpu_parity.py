@@ -18,6 +18,7 @@ from oracle.params import GeneratedParams
 from synth import gen, native, workloads
 from synth.device import DeviceInputs
 
+import gpu_common
 from gpu_common import TIERS, MkRun, check_close, check_logits, check_tokens, compare_activations, tier_of
 
 pytestmark = pytest.mark.gpu
@@ -184,6 +185,114 @@ def test_8b_shapes_2_layers_b32_mfma_all_activations():
     ref, inter = od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
     _check_step(w, logits, ref)
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
+UNFUSED_CASES = {
+    "tiny_f32": workloads.tiny().replace(unfused=1, name="tiny_unfused"),
+    "tiny_bf16_b3": workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1, batch=3,
+                                             kv_len=(128, 41, 97), n_q_heads=8, gemv_tiles=5, kv_chunk=24,
+                                             unfused=1, name="tiny_bf16_b3_unfused"),
+    "mfma_b32": workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, batch=32,
+                                         kv_len=(128,) * 32, kv_capacity=128, gemv_tiles=8, unfused=1,
+                                         name="tiny_mfma_b32_unfused"),
+}
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic", "levels", "per_op"])
+@pytest.mark.parametrize("case", list(UNFUSED_CASES))
+def test_unfused_graph_all_activations(case, mode):
+    # The graph lowered without the epilogue-fusion pass: standalone RMSNORM tasks
+    # (one per row, FUSED_RESIDUAL carrying the residual adds), GEMVs with no norm or
+    # residual flag.  Every activation, including the unfused graph's own buffers
+    # (normed inputs, o and down projections before their residual), against the oracle.
+    w = UNFUSED_CASES[case]
+    _say(f"unfused graph {case}, {mode}")
+    run = MkRun(w)
+    if mode != "per_op":
+        run.graph.mk_set_schedule(SCHED[mode])
+    logits = run.step("per_op" if mode == "per_op" else "persistent")
+    ref, inter = _oracle(w, keep=True)
+    compare_activations(w, run.activations(), inter, range(w.batch))
+    _check_step(w, logits, ref)
+    run.close()
+
+
+def test_unfused_8b_shapes_2_layers():
+    # RMSNORM tasks at hidden 4096 with the 8B-class batch-1 GEMV specialisation.
+    w = workloads.get("8b_b1").replace(n_layers=2, kv_len=(256,), kv_capacity=256, unfused=1,
+                                       name="8b_shapes_l2_unfused")
+    _say("8B shapes, 2 layers, batch 1, unfused graph, all activations")
+    run = MkRun(w)
+    assert run.graph.mk_graph_kernel_name() == "h4096_i14336_b1"
+    logits = run.step("persistent")
+    p = GeneratedParams(w, backend="c")
+    ref, inter = od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), keep=True)
+    compare_activations(w, run.activations(), inter, range(w.batch))
+    _check_step(w, logits, ref)
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic", "levels", "per_op"])
+def test_sample_tasks_one_step(mode):
+    # SAMPLE tasks at the end of the graph: one launch gives the logits, each row's
+    # greedy token in tokens and the next positions.
+    w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1, batch=3,
+                                 kv_len=(128, 41, 97), kv_capacity=160, n_q_heads=8, gemv_tiles=5, kv_chunk=24,
+                                 sample=1, name="tiny_bf16_b3_sample")
+    _say(f"tiny bf16 batch 3 with SAMPLE tasks, {mode}")
+    run = MkRun(w)
+    if mode != "per_op":
+        run.graph.mk_set_schedule(SCHED[mode])
+    logits = run.step("per_op" if mode == "per_op" else "persistent")
+    ref, _ = _oracle(w)
+    _, toks, ref_toks = _check_step(w, logits, ref)
+    assert run.inp.tokens.cpu().tolist() == toks == ref_toks
+    assert run.inp.positions.cpu().tolist() == (w.positions() + 1).tolist()
+    run.close()
+
+
+@pytest.mark.parametrize("name,steps", [("tiny", 8), ("1b_b1", 4)])
+def test_sample_graph_greedy_loop_one_launch_per_token(name, steps):
+    # mk_decode_greedy on a graph with SAMPLE tasks: one launch per token, tokens and
+    # positions updated on the device; every token against the oracle's greedy loop.
+    w = workloads.get(name).replace(sample=1).with_steps(steps)
+    _say(f"{name}: {steps} greedy steps, SAMPLE in the graph (one launch per token)")
+    run = MkRun(w)
+    p = GeneratedParams(w, backend="c" if name != "tiny" else "auto")
+    kv = od.KVState(p)
+    tok, pos = w.tokens(), workloads.get(name).positions()
+    run.inp.set_step(tok, pos)
+    out = torch.full((steps * w.batch,), -1, dtype=torch.int32, device="cuda")
+    run.graph.mk_decode_greedy(run.stream, steps, *run.inp.step_ptrs(), out.data_ptr())
+    assert run.graph.mk_status() == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(steps, w.batch)
+    tol = TIERS[tier_of(w)]
+    diverged = False
+    for s in range(steps):
+        ref, _ = od.decode_step(w, p, tok, pos, kv)
+        ref_t = [od.greedy_token(r) for r in ref]
+        margin = min(od.top2_margin(r) for r in ref)
+        _say(f"{name} step {s}: device tokens {got[s].tolist()} oracle {ref_t} (top-2 margin {margin:.2e})")
+        if got[s].tolist() != ref_t:
+            # only a near-tie of the oracle may differ; the two sequences part there
+            for b in range(w.batch):
+                if got[s][b] != ref_t[b]:
+                    assert od.top2_margin(ref[b]) < gpu_common.tie_bound(ref[b], tol), (s, b)
+                    assert ref[b][ref_t[b]] - ref[b][got[s][b]] <= gpu_common.tie_bound(ref[b], tol), (s, b)
+            diverged = True
+            break
+        tok = np.array(ref_t, dtype=np.int32)
+        pos = pos + 1
+    if not diverged:
+        check_logits(run.inp.logits.cpu().numpy().astype(np.float64), ref, w, "logits of the last step")
+        assert run.inp.positions.cpu().tolist() == pos.tolist()
+    assert run.inp.tokens.cpu().tolist() == got[-1].tolist()
     run.close()
     del run
     torch.cuda.empty_cache()
