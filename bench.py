@@ -117,7 +117,8 @@ KERNEL_SRC = os.path.join(ROOT, "task_graph_interpreter_amd", "csrc")
 # The sources the persistent kernel is compiled from (kern_spec.hip and what it
 # includes, the specialisation list, and the ABI header that fixes the descriptor
 # layout); host-only files (lowering, scheduling, runtime) do not change it.
-KERNEL_FILES = ["kern_spec.hip", "kernels.h", "tasks.h", "task_gemv.h", "task_gemv_mfma.h", "task_attn.h",
+KERNEL_FILES = ["kern_spec.hip", "kernels.h", "tasks.h", "task_gemv.h", "task_gemv_mfma.h", "task_gemv_mfma_small.h",
+                "task_attn.h",
                 "device_common.h", "specs.def", os.path.join("..", "..", "include", "mk.h")]
 
 

@@ -25,7 +25,7 @@ template <bool WBF16_, bool KVBF16_, int BM_, int KBA_, int KBD_>
 struct Spec {
   static constexpr bool WBF16 = WBF16_;    // weights bf16 (else fp32)
   static constexpr bool KVBF16 = KVBF16_;  // KV cache bf16 (else fp32)
-  static constexpr int BM = BM_;           // batch rows per GEMV pass (1 or 8); 32: MFMA tiles
+  static constexpr int BM = BM_;           // batch rows per GEMV pass (1 or 8); MFMA tiles: 16 (batch <= 8), 32
   static constexpr int KBA = KBA_;         // kblocks of K = hidden (0: generic)
   static constexpr int KBD = KBD_;         // kblocks of K = intermediate (0: generic)
 };
@@ -51,6 +51,9 @@ __device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& 
   if constexpr (S::BM == 32) {  // batched tiles on the matrix cores (every GEMV of the graph)
     gemv_mfma(a, d, t, sm);
     return;
+  } else if constexpr (S::BM == 16) {  // small-batch tiles on the matrix cores (batch <= 8)
+    gemv_mfma_small(a, d, t, sm);
+    return;
   }
   constexpr int VEC = S::WBF16 ? 8 : 4;
   const int kb = (d.k / VEC + 63) >> 6;
@@ -65,7 +68,7 @@ __device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& 
 // prefetch was issued (the tile then skips its own).
 template <class S>
 __device__ __forceinline__ bool gemv_spec_prefetch(const LaunchArgs& a, const mk_task_t& dn, int lds_used, Smem& sm) {
-  if constexpr (S::BM == 32) {
+  if constexpr (S::BM == 32 || S::BM == 16) {
     return false;
   } else {
     if (dn.op_id != MK_OP_GEMV) return false;

@@ -49,7 +49,7 @@ static int kblocks(int K, bool bf16) { return (K * (bf16 ? 2 : 4) / 16 + 63) / 6
 // one of the same dtypes and batch block.
 static const SpecEntry* select_spec(const mk_model_cfg& c) {
   const bool wb = c.weight_dtype == MK_DTYPE_BF16, kb = c.kv_dtype == MK_DTYPE_BF16;
-  const int bm = c.gemv_config == MK_GEMV_BF16_MFMA ? 32 : (c.batch == 1 ? 1 : 8);
+  const int bm = c.gemv_config == MK_GEMV_BF16_MFMA ? (c.batch <= 8 ? 16 : 32) : (c.batch == 1 ? 1 : 8);
   const int ka = kblocks(c.hidden, wb), kd = kblocks(c.intermediate, wb);
   const SpecEntry* generic = nullptr;
   for (const SpecEntry& s : kSpecs) {

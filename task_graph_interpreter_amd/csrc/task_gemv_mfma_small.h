@@ -1,0 +1,241 @@
+// GEMV task body on the matrix cores for a small batch (B <= 8 rows), descriptor
+// config_id MK_GEMV_BF16_MFMA.  Same operation as the streaming GEMV ("Mega kernel
+// initial", lowering section: one task per output-column tile; descriptor section:
+// flags SILU_MUL, ADD_RESIDUAL, RMS_NORM_INPUT):
+//   y[b, c] = r_b * sum_k (x[b, k] gamma_k) W[c, k]   (+ res[b, c]; SiLU pairs)
+//
+// Why the matrix cores at B = 8: each 16 weight bytes (8 bf16) meet 8 batch rows, 64
+// fp32 FMAs; streaming 8 TB/s of weights that way needs about 4 x 10^15 FMA/s...
+// per CU about 125 G FMA/s against the 154 G FMA/s a CU's SIMDs issue without packed
+// fp32 math, before any conversion or LDS traffic.  One v_mfma_f32_16x16x32_bf16 does
+// the 16 x 32 x 16 block in one instruction.
+//
+// Operand layout (D[16 x 16] += A[16 x 32] B[32 x 16]):
+//  * A = 16 weight rows x 32 k: lane l holds row l % 16, k = 8 (l / 16) .. +8, one
+//    16-byte load from the row-major weights;
+//  * B = 32 k x 16 columns: columns 0..7 hold the bf16 "hi" parts of the 8 batch rows'
+//    input, columns 8..15 their "lo" parts (u = x gamma = hi + lo, hi = bf16(u),
+//    lo = bf16(u - hi): the input keeps about 16 significant bits), so ONE product
+//    per block and k-step gives W hi and W lo side by side; lane l builds column l % 16
+//    for k = 8 (l / 16) .. +8.  Lanes l and l ^ 8 need the same 8 input values: each
+//    loads 4 of them (16 bytes) and takes the other 4 from its partner with a DPP move;
+//  * D: lane l holds column l % 16 of rows 4 (l / 16) .. +4;  y[b, row] sums columns
+//    b and b + 8.
+//
+// Work split, with no workgroup barrier in the streaming loop: K is cut into 8 equal
+// segments, one per wave, and every wave runs all the tile's 16-row blocks (in groups
+// of G, SiLU gate/up blocks interleaved so a pair stays in one group) over its own
+// segment, with a ring of D k-steps of weight, input and gamma loads in flight (the
+// weight ring of the first group is issued before the dependency wait).  The input is
+// a whole activation buffer every producer has finished, so after the wait it is read
+// with plain, L2-cached loads following one agent-scope acquire: the 32 CUs of an XCD
+// share it through their L2.  Per group, the 8 waves' partial products meet once in
+// LDS, and the epilogue (r_b, residual, SiLU * up) writes y.
+#pragma once
+
+#include "device_common.h"
+#include "task_gemv_mfma.h"
+
+namespace mk {
+
+// Weight row offset of lane `lane` in block gb, k-step s of the wave's segment
+// starting at k0 (bytes; kPastEnd past the segment: reads nothing).
+__device__ __forceinline__ uint32_t mfma_small_woff(const MfmaGeom& g, int gb, int k0, int s, int nst, int lane) {
+  const uint32_t row = (uint32_t)(mfma_block_row(g, gb) + (lane & 15));
+  const uint32_t k = (uint32_t)(k0 + 32 * s + 8 * (lane >> 4));
+  return s < nst ? (row * g.K + k) * 2u : kPastEnd;
+}
+
+template <int G, int D>
+__device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm,
+                                                 const MfmaGeom& g, int gb0, bool first, const char* aux, float* y,
+                                                 __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t xrs,
+                                                 __amdgpu_buffer_rsrc_t grs, bool need_ss) {
+  const int lane = lane_id(), w = wave_id();
+  const int B = d.m, N = d.n;
+  const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
+  const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
+  const int seg = (int)g.K / kWaves;  // k per wave, a multiple of 32
+  const int nst = seg / 32;
+  const int k0 = w * seg;
+  const int colj = lane & 15, kq = lane >> 4, bb = colj & 7;
+  const bool lo_lane = colj >= 8;
+  // Input: this lane's 4 of the 8 values of batch row bb at k = k0 + 32 s + 8 kq
+  // (+4 on the "lo" lanes); rows past the batch read nothing (zeros).
+  const uint32_t xbase = (uint32_t)bb * g.K * 4u + (uint32_t)(k0 + 8 * kq + (lo_lane ? 4 : 0)) * 4u;
+  auto xoff = [&](int s) -> uint32_t { return (s < nst && bb < B) ? xbase + (uint32_t)s * 128u : kPastEnd; };
+  const uint32_t gbase = (uint32_t)(k0 + 8 * kq) * 2u;
+  auto goff = [&](int s) -> uint32_t { return s < nst ? gbase + (uint32_t)s * 64u : kPastEnd; };
+
+  u32x4 wr[D][G];
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd)
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, dd, nst, lane), 0,
+                                                        kCachePolicyNT);
+  if (first) {
+    if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
+    // The input is read with plain loads: drop stale L1/L2 lines first.
+    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+  }
+  u32x4 xr[D], gr[D];
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd) {
+    xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(dd), 0, 0);
+    gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(dd), 0, 0);
+  }
+  f32x4 acc[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  for (int s0 = 0; s0 < nst; s0 += D) {
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) {
+      const int sn = s0 + dd + D;  // the step this ring slot is refilled with
+      // Assemble the 8 input values of this lane's column: its own 4 and its
+      // partner's (lane ^ 8).
+      float xv[8];
+      {
+        const u32x4 mine = xr[dd];
+        const float m0 = __uint_as_float(mine.x), m1 = __uint_as_float(mine.y);
+        const float m2 = __uint_as_float(mine.z), m3 = __uint_as_float(mine.w);
+        const float p0 = lane_xor<8>(m0), p1 = lane_xor<8>(m1), p2 = lane_xor<8>(m2), p3 = lane_xor<8>(m3);
+        xv[0] = lo_lane ? p0 : m0; xv[1] = lo_lane ? p1 : m1; xv[2] = lo_lane ? p2 : m2; xv[3] = lo_lane ? p3 : m3;
+        xv[4] = lo_lane ? m0 : p0; xv[5] = lo_lane ? m1 : p1; xv[6] = lo_lane ? m2 : p2; xv[7] = lo_lane ? m3 : p3;
+      }
+      float gv[8];
+      {
+        const u32x4 gg = gr[dd];
+        gv[0] = bf16_lo(gg.x); gv[1] = bf16_hi(gg.x); gv[2] = bf16_lo(gg.y); gv[3] = bf16_hi(gg.y);
+        gv[4] = bf16_lo(gg.z); gv[5] = bf16_hi(gg.z); gv[6] = bf16_lo(gg.w); gv[7] = bf16_hi(gg.w);
+      }
+      // Keep the refills after the reads of the same slots, so each slot stays in its
+      // registers across iterations.
+      xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
+      gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(sn), 0, 0);
+      uint32_t bw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u0 = norm ? xv[2 * e] * gv[2 * e] : xv[2 * e];
+        const float u1 = norm ? xv[2 * e + 1] * gv[2 * e + 1] : xv[2 * e + 1];
+        ss = fmaf(xv[2 * e], xv[2 * e], fmaf(xv[2 * e + 1], xv[2 * e + 1], ss));
+        const uint16_t h0 = f32_to_bf16_rne(u0), h1 = f32_to_bf16_rne(u1);
+        const uint16_t l0 = f32_to_bf16_rne(u0 - __uint_as_float((uint32_t)h0 << 16));
+        const uint16_t l1 = f32_to_bf16_rne(u1 - __uint_as_float((uint32_t)h1 << 16));
+        bw[e] = lo_lane ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : ((uint32_t)h0 | ((uint32_t)h1 << 16));
+      }
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        // The product first, then the refill of the same ring slot: the new load can
+        // land in the registers the product has read, so the ring never needs copying
+        // (a copy of a register with a load in flight would wait for every load).
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[dd][r]), bop, acc[r], 0, 0, 0);
+        wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, sn, nst, lane), 0,
+                                                          kCachePolicyNT);
+      }
+      // Keep each step's loads in its own step: the scheduler would otherwise gather
+      // them at the end of the unrolled body, where they all drain before the next.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // Sum of squares of each batch row over this wave's segment: the "hi" lanes (columns
+  // 0..7) of the four k-quarters hold every value once.
+  float* part = sm.xs;                       // [kWaves][G][64 lanes] f32x4
+  float* row_ss = sm.red + kRedFloats - 128;  // [kWaves][8]
+  if (need_ss) {
+    ss = lo_lane ? 0.f : ss;
+    ss += lane_xor<16>(ss);
+    ss += lane_xor<32>(ss);
+    if (lane < 8) row_ss[w * 8 + lane] = ss;
+  }
+#pragma unroll
+  for (int r = 0; r < G; ++r) *(f32x4*)(part + ((w * G + r) * 64 + lane) * 4) = acc[r];
+  __syncthreads();
+
+  // Epilogue: element e = (block or SiLU pair q, row n of the block, batch row b).
+  const int per = g.silu ? G / 2 : G;
+  const int nel = per * 16 * B;
+  for (int e = threadIdx.x; e < nel; e += kThreads) {
+    const int q = e / (16 * B), rem = e - q * 16 * B, n = rem / B, b = rem - n * B;
+    const int lh = (n >> 2) * 16 + b, ll = lh + 8, tt = n & 3;
+    auto sum_block = [&](int r) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float* pr = part + (ww * G + r) * 64 * 4;
+        s += pr[lh * 4 + tt] + pr[ll * 4 + tt];
+      }
+      return s;
+    };
+    float scale = 1.f;
+    if (norm) {
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) tot += row_ss[ww * 8 + b];
+      scale = 1.0f / sqrtf(tot / (float)g.K + a.rms_eps);
+    }
+    float v;
+    int col;
+    if (g.silu) {
+      const float gt = sum_block(2 * q) * scale, up = sum_block(2 * q + 1) * scale;
+      v = gt / (1.f + __expf(-gt)) * up;
+      col = g.c0 + 16 * ((gb0 >> 1) + q) + n;
+    } else {
+      v = sum_block(q) * scale;
+      col = g.c0 + 16 * (gb0 + q) + n;
+    }
+    const size_t o = (size_t)b * N + col;
+    st_dev<float>(y, o, v + (resid ? ld_dev<float>(aux, o) : 0.f));
+  }
+  __syncthreads();  // the partial-sum area and the row sums are read by every thread
+  return true;
+}
+
+__device__ __forceinline__ void gemv_mfma_small(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  MfmaGeom g;
+  g.W = resolve(a, d.in_buf[1]);
+  g.K = (uint32_t)d.k;
+  g.c0 = (int)d.reserved[0];
+  g.cols = (int)d.reserved[1];
+  g.I = (int)d.reserved[2];
+  g.silu = (d.flags & MK_FLAG_SILU_MUL) ? 1 : 0;
+  g.nc = 0;
+  const char* x = resolve(a, d.in_buf[0]);
+  const char* aux = d.in_buf[2] != 0xFFFF ? resolve(a, d.in_buf[2]) : nullptr;
+  float* y = (float*)resolve(a, d.out_buf);
+  const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, (short)0, (int)kWeightRange, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((uint32_t)d.m * g.K * 4u), kRawBufferWord3);
+  // Without the norm the gamma resource has range 0: its loads (unconditional, so the
+  // streaming loop has no branch) read nothing and return zeros, which are not used.
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(norm ? aux : x), (short)0, (int)(norm ? g.K * 2u : 0u), kRawBufferWord3);
+  const int R = (g.cols >> 4) << g.silu;  // blocks of 16 weight rows
+  bool first = true;
+  for (int gb0 = 0; gb0 < R;) {
+    const int left = R - gb0;
+    bool ok;
+    if (left >= 8) {
+      ok = mfma_small_group<8, 2>(a, d, t, sm, g, gb0, first, aux, y, wrs, xrs, grs, first);
+      gb0 += 8;
+    } else if (left >= 4) {
+      ok = mfma_small_group<4, 4>(a, d, t, sm, g, gb0, first, aux, y, wrs, xrs, grs, first);
+      gb0 += 4;
+    } else if (left >= 2) {
+      ok = mfma_small_group<2, 8>(a, d, t, sm, g, gb0, first, aux, y, wrs, xrs, grs, first);
+      gb0 += 2;
+    } else {
+      ok = mfma_small_group<1, 8>(a, d, t, sm, g, gb0, first, aux, y, wrs, xrs, grs, first);
+      gb0 += 1;
+    }
+    if (!ok) return;
+    first = false;
+  }
+}
+
+}  // namespace mk

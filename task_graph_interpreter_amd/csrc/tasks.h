@@ -11,6 +11,7 @@
 #include "task_attn.h"
 #include "task_gemv.h"
 #include "task_gemv_mfma.h"
+#include "task_gemv_mfma_small.h"
 
 namespace mk {
 

@@ -151,6 +151,12 @@ MFMA_CASES = {
     # in steady state (several chunks per group)
     "b32_wide": dict(batch=32, kv_len=(128,) * 32, hidden=1024, n_q_heads=16, n_kv_heads=4, intermediate=2048,
                      gemv_tiles=24, kv_chunk=64),
+    # batch <= 8 runs the small-batch matrix-core tile: a full batch of 8, ragged;
+    # wider layers with groups of 8, 4, 2 and 1 blocks and several k-steps per wave
+    "b8": dict(batch=8, kv_len=tuple(40 + 11 * i for i in range(8)), gemv_tiles=8, kv_chunk=32),
+    "b8_wide": dict(batch=8, kv_len=(128,) * 8, hidden=2048, n_q_heads=16, n_kv_heads=4, intermediate=4096,
+                    gemv_tiles=12, kv_chunk=64),
+    "b1": dict(batch=1, kv_len=(128,), gemv_tiles=7, kv_chunk=32),
 }
 
 
@@ -162,7 +168,7 @@ def test_tiny_mfma_gemv_all_activations(case):
                                  name=f"tiny_mfma_{case}", **MFMA_CASES[case])
     _say(f"tiny MFMA GEMV {case}")
     run = MkRun(w)
-    assert run.graph.mk_graph_kernel_name().startswith("mfma_")
+    assert run.graph.mk_graph_kernel_name().startswith("mfma8_" if w.batch <= 8 else "mfma_")
     logits = run.step("persistent")
     ref, inter = _oracle(w, keep=True)
     compare_activations(w, run.activations(), inter, range(w.batch))
@@ -293,6 +299,26 @@ def test_sample_graph_greedy_loop_one_launch_per_token(name, steps):
         check_logits(run.inp.logits.cpu().numpy().astype(np.float64), ref, w, "logits of the last step")
         assert run.inp.positions.cpu().tolist() == pos.tolist()
     assert run.inp.tokens.cpu().tolist() == got[-1].tolist()
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+
+def test_8b_shapes_2_layers_b8_mfma_all_activations():
+    # The small-batch matrix-core tile at the 8B-class layer shapes (K = 4096 and
+    # 14336 split over 8 waves: 16 and 56 k-steps each; o and down tiles of one block,
+    # gate_up tiles of 6 and 8 interleaved blocks, lm_head groups of 8, 4, 2 and 1),
+    # 2 layers, batch 8 with ragged lengths, every activation against the oracle.
+    w = workloads.get("8b_b8_ragged").replace(n_layers=2, name="8b_shapes_l2_b8")
+    _say("8B shapes, 2 layers, batch 8 ragged, small-batch MFMA GEMV, all activations")
+    run = MkRun(w)
+    assert run.graph.mk_graph_kernel_name() == "mfma8_bf16_bf16"
+    logits = run.step("persistent")
+    p = GeneratedParams(w, backend="c")
+    ref, inter = od.decode_step(w, p, w.tokens(), w.positions(), od.KVState(p), keep=True)
+    compare_activations(w, run.activations(), inter, range(w.batch))
+    _check_step(w, logits, ref)
+    assert np.array_equal(run.step("per_op"), logits), "per-op and persistent paths differ"
     run.close()
     del run
     torch.cuda.empty_cache()
