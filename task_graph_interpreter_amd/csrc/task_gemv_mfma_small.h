@@ -22,11 +22,11 @@
 //  * D: lane l holds column l % 16 of rows 4 (l / 16) .. +4;  y[b, row] sums columns
 //    b and b + 8.
 //
-// Work split, with no workgroup barrier in the streaming loop: K is cut into 8 equal
-// segments, one per wave, and every wave runs all the tile's 16-row blocks (in groups
-// of G, SiLU gate/up blocks interleaved so a pair stays in one group) over its own
-// segment, with a ring of D k-steps of weight, input and gamma loads in flight (the
-// weight ring of the first group is issued before the dependency wait).  The input is
+// Work split, with no workgroup barrier in the streaming loop: the k-steps of 32 are
+// dealt to the 8 waves round robin, and every wave runs all the tile's 16-row blocks
+// (in groups of G, SiLU gate/up blocks interleaved so a pair stays in one group) over
+// its own steps, with a ring of D k-steps of weight, input and gamma loads in flight
+// (the weight ring of the first group is issued before the dependency wait).  The input is
 // a whole activation buffer every producer has finished, so after the wait it is read
 // with plain, L2-cached loads following one agent-scope acquire: the 32 CUs of an XCD
 // share it through their L2.  Per group, the 8 waves' partial products meet once in
@@ -38,11 +38,13 @@
 
 namespace mk {
 
-// Weight row offset of lane `lane` in block gb, k-step s of the wave's segment
-// starting at k0 (bytes; kPastEnd past the segment: reads nothing).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Weight row offset of lane `lane` in block gb at the wave's k-step s, which covers
+// k = 32 (w + 8 s) .. +32 (bytes; kPastEnd past the last step: reads nothing).
 __device__ __forceinline__ uint32_t mfma_small_woff(const MfmaGeom& g, int gb, int k0, int s, int nst, int lane) {
   const uint32_t row = (uint32_t)(mfma_block_row(g, gb) + (lane & 15));
-  const uint32_t k = (uint32_t)(k0 + 32 * s + 8 * (lane >> 4));
+  const uint32_t k = (uint32_t)(k0 + 256 * s + 8 * (lane >> 4));
   return s < nst ? (row * g.K + k) * 2u : kPastEnd;
 }
 
@@ -55,25 +57,32 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   const int B = d.m, N = d.n;
   const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
-  const int seg = (int)g.K / kWaves;  // k per wave, a multiple of 32
-  const int nst = seg / 32;
-  const int k0 = w * seg;
+  // Wave w takes the k-steps w, w + 8, w + 16, ... (32 k each): at any time the 8 waves
+  // of a workgroup read 8 adjacent 64-byte pieces of the same weight rows, 512
+  // contiguous bytes per row, instead of 8 far-apart places.
+  const int nst = (int)g.K / (32 * kWaves);
+  const int k0 = 32 * w;
   const int colj = lane & 15, kq = lane >> 4, bb = colj & 7;
   const bool lo_lane = colj >= 8;
   // Input: this lane's 4 of the 8 values of batch row bb at k = k0 + 32 s + 8 kq
   // (+4 on the "lo" lanes); rows past the batch read nothing (zeros).
   const uint32_t xbase = (uint32_t)bb * g.K * 4u + (uint32_t)(k0 + 8 * kq + (lo_lane ? 4 : 0)) * 4u;
-  auto xoff = [&](int s) -> uint32_t { return (s < nst && bb < B) ? xbase + (uint32_t)s * 128u : kPastEnd; };
+  auto xoff = [&](int s) -> uint32_t { return (s < nst && bb < B) ? xbase + (uint32_t)s * 1024u : kPastEnd; };
   const uint32_t gbase = (uint32_t)(k0 + 8 * kq) * 2u;
-  auto goff = [&](int s) -> uint32_t { return s < nst ? gbase + (uint32_t)s * 64u : kPastEnd; };
+  auto goff = [&](int s) -> uint32_t { return s < nst ? gbase + (uint32_t)s * 512u : kPastEnd; };
 
+  // The ring is filled in the order the loop consumes and refills it (each slot's
+  // loads kept together by a scheduling barrier): the wait counts the compiler places
+  // at the loop head then hold on entry too, instead of draining every load.
   u32x4 wr[D][G];
 #pragma unroll
-  for (int dd = 0; dd < D; ++dd)
+  for (int dd = 0; dd < D; ++dd) {
 #pragma unroll
     for (int r = 0; r < G; ++r)
       wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, dd, nst, lane), 0,
                                                         kCachePolicyNT);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (first) {
     if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
     // The input is read with plain loads: drop stale L1/L2 lines first.
@@ -85,61 +94,72 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   for (int dd = 0; dd < D; ++dd) {
     xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(dd), 0, 0);
     gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(dd), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   f32x4 acc[G];
 #pragma unroll
   for (int r = 0; r < G; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
-  for (int s0 = 0; s0 < nst; s0 += D) {
-#pragma unroll
-    for (int dd = 0; dd < D; ++dd) {
-      const int sn = s0 + dd + D;  // the step this ring slot is refilled with
-      // Assemble the 8 input values of this lane's column: its own 4 and its
-      // partner's (lane ^ 8).
-      float xv[8];
-      {
-        const u32x4 mine = xr[dd];
-        const float m0 = __uint_as_float(mine.x), m1 = __uint_as_float(mine.y);
-        const float m2 = __uint_as_float(mine.z), m3 = __uint_as_float(mine.w);
-        const float p0 = lane_xor<8>(m0), p1 = lane_xor<8>(m1), p2 = lane_xor<8>(m2), p3 = lane_xor<8>(m3);
-        xv[0] = lo_lane ? p0 : m0; xv[1] = lo_lane ? p1 : m1; xv[2] = lo_lane ? p2 : m2; xv[3] = lo_lane ? p3 : m3;
-        xv[4] = lo_lane ? m0 : p0; xv[5] = lo_lane ? m1 : p1; xv[6] = lo_lane ? m2 : p2; xv[7] = lo_lane ? m3 : p3;
-      }
-      float gv[8];
-      {
-        const u32x4 gg = gr[dd];
-        gv[0] = bf16_lo(gg.x); gv[1] = bf16_hi(gg.x); gv[2] = bf16_lo(gg.y); gv[3] = bf16_hi(gg.y);
-        gv[4] = bf16_lo(gg.z); gv[5] = bf16_hi(gg.z); gv[6] = bf16_lo(gg.w); gv[7] = bf16_hi(gg.w);
-      }
-      // Keep the refills after the reads of the same slots, so each slot stays in its
-      // registers across iterations.
-      xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
-      gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(sn), 0, 0);
-      uint32_t bw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float u0 = norm ? xv[2 * e] * gv[2 * e] : xv[2 * e];
-        const float u1 = norm ? xv[2 * e + 1] * gv[2 * e + 1] : xv[2 * e + 1];
-        ss = fmaf(xv[2 * e], xv[2 * e], fmaf(xv[2 * e + 1], xv[2 * e + 1], ss));
-        const uint16_t h0 = f32_to_bf16_rne(u0), h1 = f32_to_bf16_rne(u1);
-        const uint16_t l0 = f32_to_bf16_rne(u0 - __uint_as_float((uint32_t)h0 << 16));
-        const uint16_t l1 = f32_to_bf16_rne(u1 - __uint_as_float((uint32_t)h1 << 16));
-        bw[e] = lo_lane ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : ((uint32_t)h0 | ((uint32_t)h1 << 16));
-      }
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        // The product first, then the refill of the same ring slot: the new load can
-        // land in the registers the product has read, so the ring never needs copying
-        // (a copy of a register with a load in flight would wait for every load).
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[dd][r]), bop, acc[r], 0, 0, 0);
-        wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, sn, nst, lane), 0,
-                                                          kCachePolicyNT);
-      }
-      // Keep each step's loads in its own step: the scheduler would otherwise gather
-      // them at the end of the unrolled body, where they all drain before the next.
-      __builtin_amdgcn_sched_barrier(0);
+  // One k-step from ring slot dd (steps s0 + dd; the slot is refilled with s0 + dd + D).
+  auto step = [&](int dd, int s0) __attribute__((always_inline)) {
+    const int sn = s0 + dd + D;
+    // Assemble the 8 input values of this lane's column: its own 4 and its partner's
+    // (lane ^ 8).
+    float xv[8];
+    {
+      const u32x4 mine = xr[dd];
+      const float m0 = __uint_as_float(mine.x), m1 = __uint_as_float(mine.y);
+      const float m2 = __uint_as_float(mine.z), m3 = __uint_as_float(mine.w);
+      const float p0 = lane_xor<8>(m0), p1 = lane_xor<8>(m1), p2 = lane_xor<8>(m2), p3 = lane_xor<8>(m3);
+      xv[0] = lo_lane ? p0 : m0; xv[1] = lo_lane ? p1 : m1; xv[2] = lo_lane ? p2 : m2; xv[3] = lo_lane ? p3 : m3;
+      xv[4] = lo_lane ? m0 : p0; xv[5] = lo_lane ? m1 : p1; xv[6] = lo_lane ? m2 : p2; xv[7] = lo_lane ? m3 : p3;
     }
+    float gv[8];
+    {
+      const u32x4 gg = gr[dd];
+      gv[0] = bf16_lo(gg.x); gv[1] = bf16_hi(gg.x); gv[2] = bf16_lo(gg.y); gv[3] = bf16_hi(gg.y);
+      gv[4] = bf16_lo(gg.z); gv[5] = bf16_hi(gg.z); gv[6] = bf16_lo(gg.w); gv[7] = bf16_hi(gg.w);
+    }
+    // Every read of the slots' old values is done before they are refilled, so the
+    // refills land in the same registers (no copies, whose waits would drain the ring):
+    // the unpacked values are pinned in registers first.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(xv[e]), "+v"(gv[e]));
+    __builtin_amdgcn_sched_barrier(0);
+    xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
+    gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(sn), 0, 0);
+    uint32_t bw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float u0 = norm ? xv[2 * e] * gv[2 * e] : xv[2 * e];
+      const float u1 = norm ? xv[2 * e + 1] * gv[2 * e + 1] : xv[2 * e + 1];
+      ss = fmaf(xv[2 * e], xv[2 * e], fmaf(xv[2 * e + 1], xv[2 * e + 1], ss));
+      // hi = bf16(u) (round to nearest even), lo = bf16(u - hi)
+      const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)u0, (__bf16)u1});
+      const float r0 = u0 - __uint_as_float(h << 16), r1 = u1 - __uint_as_float(h & 0xFFFF0000u);
+      const uint32_t l = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)r0, (__bf16)r1});
+      bw[e] = lo_lane ? l : h;
+    }
+    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      // The product first, then the refill of the same ring slot: the new load can
+      // land in the registers the product has read, so the ring never needs copying.
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[dd][r]), bop, acc[r], 0, 0, 0);
+      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, sn, nst, lane), 0,
+                                                        kCachePolicyNT);
+    }
+    // Keep each step's loads in its own step: the scheduler would otherwise gather
+    // them at the end of the unrolled body, where they all drain before the next.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The first D steps run outside the loop: they leave the ring in the order the loop
+  // refills it, so the wait counts at the loop head are exact on entry as well.
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd) step(dd, 0);
+  for (int s0 = D; s0 < nst; s0 += D) {
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) step(dd, s0);
   }
   // Sum of squares of each batch row over this wave's segment: the "hi" lanes (columns
   // 0..7) of the four k-quarters hold every value once.
