@@ -243,7 +243,7 @@ def timed(fn, steps, warmup, stream, ptrs):
 def model_key(w):
     """Workloads with equal keys have bitwise-equal weights (same shapes and seed)."""
     return (w.n_layers, w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.intermediate, w.vocab, w.weight_dtype,
-            w.seed)
+            w.seed, w.packed)
 
 
 def time_other_workload(name, steps, warmup, stream, shared):
@@ -261,6 +261,8 @@ def time_other_workload(name, steps, warmup, stream, shared):
     reuse = shared is not None and shared[0] == model_key(w)
     log(f"{name}: filling inputs" + (" (weights shared)" if reuse else ""))
     inp = DeviceInputs(w, weights=shared[1] if reuse else None)
+    if w.packed and not reuse:
+        inp.weights = inp.packed_weights()  # one-time load-time layout change, not timed
     cfg, keep = mk.make_cfg(**w.mk_fields())
     plan = mk.mk_plan(cfg)
     scratch = torch.zeros(plan["scratch_bytes"], dtype=torch.uint8, device="cuda")
@@ -279,7 +281,8 @@ def time_other_workload(name, steps, warmup, stream, shared):
     ms, ms2 = total / steps, t2 / steps
     achieved = w.bytes_per_step() / (ms / 1e3) / 1e9
     out = {"workload": name, "batch": w.batch, "kv_len": list(w.kv_len), "kv_chunk": w.kv_chunk,
-           "gemv_config": w.gemv_config, "kernel": g.mk_graph_kernel_name(), "ms_per_step": ms,
+           "gemv_config": w.gemv_config, "kernel": g.mk_graph_kernel_name(),
+           "weight_layout": "tile16" if w.packed else "row-major", "ms_per_step": ms,
            "latency_ms_median": float(np.median(per)), "tokens_per_s": w.batch * steps / (total / 1e3),
            "bytes_per_step": w.bytes_per_step(), "achieved_gbs": achieved, "frac": achieved / PEAK_HBM_GBS,
            "traffic": measured_traffic(name), "per_op_ms_per_step": ms2, "speedup_over_per_op": ms2 / ms}
@@ -350,6 +353,11 @@ def main():
     torch.cuda.set_device(0)
     log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
     inp = DeviceInputs(w)
+    if w.packed:
+        # Matrices into the tile layout of mk_pack_matrix (a one-time conversion when the
+        # weights are loaded, not timed); the row-major copies are dropped.
+        inp.weights = inp.packed_weights()
+        torch.cuda.synchronize()
     cfg, keep = mk.make_cfg(**w.mk_fields())
     plan = mk.mk_plan(cfg)
     n_closed, _ = og.closed_form_counts(w.replace(join_nodes=0))
@@ -516,7 +524,7 @@ def main():
                    "vocab": w.vocab, "batch": w.batch, "kv_len": list(w.kv_len)[:4], "weight_dtype": w.weight_dtype,
                    "kv_dtype": w.kv_dtype, "gemv_tiles": w.gemv_tiles, "kv_chunk": w.kv_chunk,
                    "tasks": plan["n_tasks"], "edges": plan["n_edges"], "schedule": args.schedule,
-                   "kernel": name_timed},
+                   "kernel": name_timed, "weight_layout": "tile16" if w.packed else "row-major"},
         "latency_ms": {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
                        "p90": float(np.percentile(per, 90))},
         "bytes_per_step": bytes_step,

@@ -148,6 +148,14 @@ typedef struct mk_model_cfg {
  *     and advances positions_dev: one launch runs a whole greedy step. */
 #define MK_LOWER_UNFUSED 1
 #define MK_LOWER_SAMPLE 2
+/*   MK_LOWER_PACKED_WEIGHTS: the five matrices of every layer and the lm_head (W_qkv,
+ *     W_o, W_gate_up, W_down, W_lm; not the embedding) are passed in the 16-row tile
+ *     layout that mk_pack_matrix writes.  Needs gemv_config MK_GEMV_BF16_MFMA and batch
+ *     <= 8 (the matrix-core tile for small batches reads that layout one contiguous
+ *     kilobyte per wave and k-step); MK_ERR_INVALID otherwise.  The descriptors are the
+ *     same as without the bit: the layout is a property of the weight buffers, and the
+ *     results are bitwise those of the row-major weights. */
+#define MK_LOWER_PACKED_WEIGHTS 4
 
 /* Weights in canonical order (buffer-table section of the page: append-only, one
  * index per tensor): [0] embedding [vocab, hidden]; per layer l at 1 + 6 l:
@@ -208,6 +216,19 @@ void mk_lowered_free(mk_lowered* g);
  * *out is NULL on failure. */
 int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scratch_dev,
                    void* stream, mk_graph** out);
+
+/* Write the 16-row tile layout of one bf16 matrix, for graphs lowered with
+ * MK_LOWER_PACKED_WEIGHTS (a one-time conversion when the weights are loaded; not part
+ * of the pages' method: the matrix-core tile reads it with whole-kilobyte loads).
+ * src: device pointer, row-major [rows, cols] bf16; dst: device pointer to
+ * rows * cols * 2 bytes, not overlapping src.  Both 16-byte aligned, rows % 16 == 0,
+ * cols % 32 == 0.  Layout: for row block r (rows 16 r .. 16 r + 15) and k-step j
+ * (cols 32 j .. 32 j + 31) a 1024-byte tile at byte (r * cols / 32 + j) * 1024 holds,
+ * for lane l = 0..63, the 8 values src[16 r + l % 16][32 j + 8 (l / 16) + e], e = 0..7,
+ * at byte 16 l + 2 e.  A block of 16 rows keeps its place (the same 32 cols bytes as
+ * row-major).  Enqueued on `stream` (asynchronous; no allocation).  Errors:
+ * MK_ERR_INVALID (sizes, NULL, overlap), MK_ERR_ALIGN, MK_ERR_HIP. */
+int mk_pack_matrix(const void* src_dev, void* dst_dev, int32_t rows, int32_t cols, void* stream);
 
 /* Host copies of what mk_build_graph uploaded (library-owned, valid until mk_destroy). */
 int mk_graph_tasks(const mk_graph* g, const mk_task_t** tasks, uint32_t* n);

@@ -51,6 +51,21 @@ class DeviceInputs:
                 native.gpu_fill_cache(cache[l].data_ptr(), w.batch * w.n_kv_heads, w.kv_capacity, w.head_dim,
                                       w.seed, w.tid_layer(l, which), 0.0, workloads.KV_STD, w.kv_dtype, stream)
 
+    def packed_weights(self):
+        """The weight list with every matrix (W_qkv, W_o, W_gate_up, W_down, W_lm) copied
+        into the library's 16-row tile layout by mk_pack_matrix, for graphs lowered with
+        MK_LOWER_PACKED_WEIGHTS; the other tensors are shared, self.weights is unchanged."""
+        from task_graph_interpreter_amd import binding as mk
+
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        out = list(self.weights)
+        for i in mk.packed_matrix_indices(self.w.n_layers):
+            src = self.weights[i]
+            dst = torch.empty_like(src)
+            mk.mk_pack_matrix(src.data_ptr(), dst.data_ptr(), src.shape[0], src.shape[1], stream)
+            out[i] = dst
+        return out
+
     def weight_ptrs(self):
         return [t.data_ptr() for t in self.weights]
 

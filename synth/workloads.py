@@ -59,6 +59,7 @@ class Workload:
     join_nodes: int = 1
     unfused: int = 0  # 1: lower without the epilogue-fusion pass (standalone RMSNORM tasks)
     sample: int = 0   # 1: SAMPLE tasks after the lm_head (a whole greedy step per launch)
+    packed: int = 0   # 1: matrices in the library's 16-row tile layout (MFMA GEMV, batch <= 8)
     seed: int = 0
     meta: dict = field(default_factory=dict, compare=False)
 
@@ -111,7 +112,7 @@ class Workload:
                     weight_dtype=self.weight_dtype, kv_dtype=self.kv_dtype, gemv_tiles=self.gemv_tiles,
                     kv_chunk=self.kv_chunk, join_nodes=self.join_nodes, gemv_config=self.gemv_config,
                     kv_capacity=self.kv_capacity, kv_len=self.kv_len,
-                    options=(1 if self.unfused else 0) | (2 if self.sample else 0))
+                    options=(1 if self.unfused else 0) | (2 if self.sample else 0) | (4 if self.packed else 0))
 
     # ---- per-step inputs ----------------------------------------------
     def tokens(self) -> np.ndarray:
@@ -191,7 +192,7 @@ def llama8b() -> Workload:
 def llama8b_ragged(seed: int = 0) -> Workload:
     kv = _ragged_lengths(seed, 8, 512, 8192)
     return llama8b().replace(name="8b_b8_ragged", batch=8, kv_chunk=512, kv_len=kv,
-                             kv_capacity=max(kv), seed=seed, gemv_config=2)
+                             kv_capacity=max(kv), seed=seed, gemv_config=2, packed=1)
 
 
 def llama8b_long() -> Workload:

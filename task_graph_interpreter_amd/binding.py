@@ -27,7 +27,7 @@ MK_STATIC_SCRATCH_BYTES = 64 << 20
  MK_OP_ATTENTION_APPEND, MK_OP_ATTENTION_PARTIAL, MK_OP_ATTENTION_COMBINE) = range(10)
 MK_FLAG_SILU_MUL, MK_FLAG_ADD_RESIDUAL, MK_FLAG_RMS_NORM_INPUT = 1, 2, 4
 MK_FLAG_FUSED_RESIDUAL = 2
-MK_LOWER_UNFUSED, MK_LOWER_SAMPLE = 1, 2
+MK_LOWER_UNFUSED, MK_LOWER_SAMPLE, MK_LOWER_PACKED_WEIGHTS = 1, 2, 4
 # numpy mirror of mk_task_t (64 bytes), for reading the descriptor array on the host.
 MK_TASK_DTYPE = np.dtype({
     "names": ["op_id", "config_id", "step", "flags", "remaining_deps", "num_dependents", "dependents_offset",
@@ -42,7 +42,7 @@ MK_DTYPE = {"f32": 0, "bf16": 1}
 # Every symbol include/mk.h declares.
 EXPORTS = ["mk_plan", "mk_lower", "mk_lowered_tasks", "mk_lowered_edges", "mk_lowered_scratch_span",
            "mk_lowered_levels", "mk_lowered_free", "mk_build_graph", "mk_graph_tasks", "mk_graph_edges", "mk_decode_step",
-           "mk_decode_step_noalloc", "mk_decode_step_per_op", "mk_sample_greedy", "mk_decode_greedy", "mk_capture_per_op_graph",
+           "mk_decode_step_noalloc", "mk_decode_step_per_op", "mk_sample_greedy", "mk_pack_matrix", "mk_decode_greedy", "mk_capture_per_op_graph",
            "mk_launch_per_op_graph", "mk_status",
            "mk_set_wait_limit", "mk_set_trace", "mk_graph_grid", "mk_graph_kernel_name", "mk_set_schedule", "mk_graph_schedule", "mk_lowered_schedule", "mk_destroy", "mk_last_error", "mk_abi_version"]
 
@@ -109,6 +109,7 @@ def lib():
         "mk_decode_step_noalloc": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "mk_decode_step_per_op": ([vp, vp, vp, vp, vp, vp, vp], i32),
         "mk_sample_greedy": ([vp, vp, vp, vp, vp], i32),
+        "mk_pack_matrix": ([vp, vp, i32, i32, vp], i32),
         "mk_decode_greedy": ([vp, vp, i32, vp, vp, vp, vp, vp, vp], i32),
         "mk_capture_per_op_graph": ([vp, vp, vp, vp, vp, vp], i32),
         "mk_launch_per_op_graph": ([vp, vp], i32),
@@ -157,6 +158,20 @@ def make_cfg(*, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate,
                    gemv_tiles, kv_chunk, join_nodes, gemv_config, kv_capacity, options,
                    ctypes.cast(kv, ctypes.POINTER(ctypes.c_int32)))
     return c, kv
+
+
+def mk_pack_matrix(src_dev: int, dst_dev: int, rows: int, cols: int, stream: int) -> None:
+    """16-row tile layout of a bf16 [rows, cols] matrix into dst (device addresses)."""
+    _check(lib().mk_pack_matrix(src_dev, dst_dev, rows, cols, stream))
+
+
+def packed_matrix_indices(n_layers: int) -> list:
+    """Indices (canonical weight order) of the matrices MK_LOWER_PACKED_WEIGHTS covers:
+    per layer W_qkv, W_o, W_gate_up, W_down, then W_lm."""
+    out = []
+    for l in range(n_layers):
+        out += [1 + 6 * l + 1, 1 + 6 * l + 2, 1 + 6 * l + 4, 1 + 6 * l + 5]
+    return out + [2 + 6 * n_layers]
 
 
 def mk_plan(cfg: MkModelCfg) -> dict:

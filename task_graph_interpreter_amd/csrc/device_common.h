@@ -70,6 +70,7 @@ struct LaunchArgs {
   Ctrl* ctrl;
   uint64_t* trace;
   int32_t* tokens_out;  // SAMPLE tasks also write their token here when non-null ([batch])
+  uint32_t wpacked;     // 1: the matrices are in the 16-row tile layout of mk_pack_matrix
   uint64_t rt[8];  // per-step bases indexed by tag
   uint32_t n_tasks;
   uint32_t epoch;

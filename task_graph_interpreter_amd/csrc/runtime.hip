@@ -112,6 +112,20 @@ __global__ __launch_bounds__(kSampleThreads) void sample_greedy_kernel(const flo
   }
 }
 
+// 16-row tile layout of a bf16 matrix (mk_pack_matrix): one thread per 16-byte piece of
+// the output, which is written in order; piece p is lane l = p % 64 of tile p / 64, the
+// tile of row block r and k-step j being number r * (cols / 32) + j.
+__global__ __launch_bounds__(256) void pack_matrix_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                          uint64_t pieces, uint32_t cols) {
+  const uint64_t steps = cols / 32;
+  for (uint64_t p = (uint64_t)blockIdx.x * 256 + threadIdx.x; p < pieces; p += (uint64_t)gridDim.x * 256) {
+    const uint64_t tile = p >> 6, l = p & 63;
+    const uint64_t r = tile / steps, j = tile - r * steps;
+    const uint64_t row = 16 * r + (l & 15), col = 32 * j + 8 * (l >> 4);
+    dst[p] = src[(row * cols + col) / 8];
+  }
+}
+
 // Activation scratch of mk_decode_step_noalloc, for callers that cannot allocate: a
 // file-scope device array, one copy per device, held until the process ends.  In host
 // code `scratch` is a host-side stand-in for the symbol, not a device address: the
@@ -232,6 +246,7 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   a.intermediate = c.intermediate;
   a.vocab = c.vocab;
   a.kv_capacity = c.kv_capacity;
+  a.wpacked = (c.options & MK_LOWER_PACKED_WEIGHTS) ? 1u : 0u;
   return a;
 }
 
@@ -583,6 +598,23 @@ int mk_sample_greedy(mk_graph* g, void* stream, const float* logits_dev, int32_t
                      tokens_dev, positions_dev, (int32_t*)nullptr, g->d_ctrl);
   HIP_TRY(hipGetLastError());
   g->last_stream = s;
+  return MK_OK;
+}
+
+int mk_pack_matrix(const void* src_dev, void* dst_dev, int32_t rows, int32_t cols, void* stream) {
+  if (!src_dev || !dst_dev) return mk::set_error(MK_ERR_INVALID, "mk_pack_matrix: NULL pointer");
+  if (rows < 16 || cols < 32 || rows % 16 || cols % 32)
+    return mk::set_error(MK_ERR_INVALID, "mk_pack_matrix: rows must be a positive multiple of 16, cols of 32");
+  if (misaligned(src_dev, 16) || misaligned(dst_dev, 16))
+    return mk::set_error(MK_ERR_ALIGN, "mk_pack_matrix: src and dst must be 16-byte aligned");
+  const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * 2u;
+  const uintptr_t s0 = (uintptr_t)src_dev, d0 = (uintptr_t)dst_dev;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return mk::set_error(MK_ERR_INVALID, "mk_pack_matrix: src and dst overlap");
+  const uint64_t pieces = bytes / 16;
+  const uint64_t blocks = (pieces + 255) / 256;
+  hipLaunchKernelGGL(mk::pack_matrix_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4*)src_dev, (uint4*)dst_dev, pieces, (uint32_t)cols);
+  HIP_TRY(hipGetLastError());
   return MK_OK;
 }
 

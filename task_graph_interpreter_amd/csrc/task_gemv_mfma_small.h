@@ -12,7 +12,9 @@
 //
 // Operand layout (D[16 x 16] += A[16 x 32] B[32 x 16]):
 //  * A = 16 weight rows x 32 k: lane l holds row l % 16, k = 8 (l / 16) .. +8, one
-//    16-byte load from the row-major weights;
+//    16-byte load: from the row-major weights, 16 rows x 64 bytes per wave load; from
+//    the 16-row tile layout (mk_pack_matrix, MK_LOWER_PACKED_WEIGHTS), one contiguous
+//    kilobyte, which streams about a fifth faster from HBM;
 //  * B = 32 k x 16 columns: columns 0..7 hold the bf16 "hi" parts of the 8 batch rows'
 //    input, columns 8..15 their "lo" parts (u = x gamma = hi + lo, hi = bf16(u),
 //    lo = bf16(u - hi): the input keeps about 16 significant bits), so ONE product
@@ -40,12 +42,18 @@ namespace mk {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Weight row offset of lane `lane` in block gb at the wave's k-step s, which covers
-// k = 32 (w + 8 s) .. +32 (bytes; kPastEnd past the last step: reads nothing).
-__device__ __forceinline__ uint32_t mfma_small_woff(const MfmaGeom& g, int gb, int k0, int s, int nst, int lane) {
-  const uint32_t row = (uint32_t)(mfma_block_row(g, gb) + (lane & 15));
-  const uint32_t k = (uint32_t)(k0 + 256 * s + 8 * (lane >> 4));
-  return s < nst ? (row * g.K + k) * 2u : kPastEnd;
+// Byte offset of lane `lane`'s 16 weight bytes of block gb at the wave's k-step s, which
+// covers k = 32 (w + 8 s) .. +32 (kPastEnd past the last step: reads nothing).  Either
+// weight layout gives the block's base (its first row times 2K bytes: a block of 16 rows
+// is 32K contiguous bytes in both) + a per-lane term + s times a per-step stride:
+//  * row-major [N, K]: lane l reads row l % 16 at k = 32 (w + 8 s) + 8 (l / 16):
+//    lane term 2K (l % 16) + 16 (l / 16) + 64 w, stride 512 bytes;
+//  * tile layout (mk_pack_matrix): k-step j of a block is one 1 KB tile at 1024 j, with
+//    lane l's 16 bytes at 16 l: lane term 16 l + 1024 w, stride 8192 bytes.  A wave's
+//    load is then one contiguous kilobyte instead of 16 half cache lines.
+__device__ __forceinline__ uint32_t mfma_small_woff(const MfmaGeom& g, int gb, uint32_t lterm, uint32_t sstride,
+                                                    int s, int nst) {
+  return s < nst ? (uint32_t)mfma_block_row(g, gb) * g.K * 2u + lterm + (uint32_t)s * sstride : kPastEnd;
 }
 
 template <int G, int D>
@@ -58,11 +66,14 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
   // Wave w takes the k-steps w, w + 8, w + 16, ... (32 k each): at any time the 8 waves
-  // of a workgroup read 8 adjacent 64-byte pieces of the same weight rows, 512
-  // contiguous bytes per row, instead of 8 far-apart places.
+  // of a workgroup read adjacent pieces of the same weight rows (row-major: 8 x 64
+  // bytes per row; tile layout: 8 adjacent kilobyte tiles) instead of 8 far-apart places.
   const int nst = (int)g.K / (32 * kWaves);
   const int k0 = 32 * w;
   const int colj = lane & 15, kq = lane >> 4, bb = colj & 7;
+  const uint32_t lterm = a.wpacked ? 16u * (uint32_t)lane + 1024u * (uint32_t)w
+                                   : 2u * g.K * (uint32_t)colj + 16u * (uint32_t)kq + 64u * (uint32_t)w;
+  const uint32_t sstride = a.wpacked ? 8192u : 512u;
   const bool lo_lane = colj >= 8;
   // Input: this lane's 4 of the 8 values of batch row bb at k = k0 + 32 s + 8 kq
   // (+4 on the "lo" lanes); rows past the batch read nothing (zeros).
@@ -79,7 +90,7 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   for (int dd = 0; dd < D; ++dd) {
 #pragma unroll
     for (int r = 0; r < G; ++r)
-      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, dd, nst, lane), 0,
+      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, lterm, sstride, dd, nst), 0,
                                                         kCachePolicyNT);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -146,7 +157,7 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
       // The product first, then the refill of the same ring slot: the new load can
       // land in the registers the product has read, so the ring never needs copying.
       acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[dd][r]), bop, acc[r], 0, 0, 0);
-      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, k0, sn, nst, lane), 0,
+      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, lterm, sstride, sn, nst), 0,
                                                         kCachePolicyNT);
     }
     // Keep each step's loads in its own step: the scheduler would otherwise gather

@@ -105,7 +105,11 @@ class MkRun:
         self.plan = mk.mk_plan(self.cfg)
         self.scratch = torch.zeros(max(self.plan["scratch_bytes"], 256), dtype=torch.uint8, device="cuda")
         self.stream = torch.cuda.current_stream().cuda_stream
-        self.graph = mk.mk_build_graph(self.cfg, self.inp.weight_ptrs(), self.scratch.data_ptr(), self.stream)
+        # Packed graphs get their own tile-layout copies of the matrices; inputs shared
+        # with a row-major run stay as they are.
+        self.weights = self.inp.packed_weights() if w.packed else self.inp.weights
+        self.graph = mk.mk_build_graph(self.cfg, [t.data_ptr() for t in self.weights], self.scratch.data_ptr(),
+                                       self.stream)
         self.lowered = mk.mk_lower(self.cfg)
         self.bi = og.BufferIndex(w)
 

@@ -124,6 +124,50 @@ def test_unknown_option_rejected():
     assert e.value.code == binding.MK_ERR_INVALID and "options" in str(e.value)
 
 
+@pytest.mark.parametrize("name", ["8b_b8_ragged", "tiny_b8"])
+def test_packed_weight_option_lowers_the_same_graph(name):
+    # MK_LOWER_PACKED_WEIGHTS changes the layout the GEMV reads its matrices in, not
+    # the graph: descriptors and edges are byte-equal to the row-major graph's.
+    if name == "tiny_b8":
+        w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, batch=8,
+                                     kv_len=(128,) * 8, packed=1)
+    else:
+        w = workloads.get(name)
+    assert w.packed
+    a = mk.mk_lower(_cfg(w)[0])
+    b = mk.mk_lower(_cfg(w.replace(packed=0))[0])
+    assert np.array_equal(a.tasks_bytes(), b.tasks_bytes())
+    assert np.array_equal(a.edges(), b.edges())
+
+
+@pytest.mark.parametrize("over", [dict(), dict(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1),
+                                  dict(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, batch=9,
+                                       kv_len=(128,) * 9)])
+def test_packed_weight_option_needs_the_small_batch_mfma_tile(over):
+    cfg, keep = _cfg(workloads.tiny().replace(packed=1), **over)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan(cfg)
+    assert e.value.code == binding.MK_ERR_INVALID and "MK_LOWER_PACKED_WEIGHTS" in str(e.value)
+
+
+def test_pack_matrix_rejects_bad_arguments_without_a_gpu():
+    # Every argument check runs before the kernel is enqueued.
+    L = binding.lib()
+    p = lambda a: ctypes.c_void_p(a)
+    big = 1 << 40
+    cases = [
+        (L.mk_pack_matrix(None, p(big), 16, 32, None), binding.MK_ERR_INVALID, "NULL"),
+        (L.mk_pack_matrix(p(big), p(2 * big), 15, 32, None), binding.MK_ERR_INVALID, "multiple of 16"),
+        (L.mk_pack_matrix(p(big), p(2 * big), 16, 48, None), binding.MK_ERR_INVALID, "multiple of 16"),
+        (L.mk_pack_matrix(p(big), p(2 * big), 0, 32, None), binding.MK_ERR_INVALID, "multiple of 16"),
+        (L.mk_pack_matrix(p(big + 8), p(2 * big), 16, 32, None), binding.MK_ERR_ALIGN, "aligned"),
+        (L.mk_pack_matrix(p(big), p(big + 1008), 16, 32, None), binding.MK_ERR_INVALID, "overlap"),
+    ]
+    for rc, code, msg in cases:
+        assert rc == code
+    assert "overlap" in mk.mk_last_error()
+
+
 def test_scratch_layout():
     w = workloads.llama8b_ragged()
     cfg, keep = _cfg(w)

@@ -178,6 +178,53 @@ def test_tiny_mfma_gemv_all_activations(case):
     run.close()
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 32), (48, 96), (208, 4096), (4096, 1024)])
+def test_pack_matrix_layout(rows, cols):
+    # mk_pack_matrix against the layout its declaration defines, written here with
+    # numpy: tile (r, j) at (r * cols / 32 + j) KiB, lane l's 8 values
+    # src[16 r + l % 16, 32 j + 8 (l / 16) + e] at byte 16 l + 2 e.  Bit-exact.
+    _say(f"mk_pack_matrix {rows} x {cols}")
+    g = torch.Generator().manual_seed(rows * 7919 + cols)
+    src = torch.randint(-32768, 32767, (rows, cols), dtype=torch.int16, generator=g)
+    d_src = src.view(torch.bfloat16).cuda()
+    d_dst = torch.empty_like(d_src)
+    mk.mk_pack_matrix(d_src.data_ptr(), d_dst.data_ptr(), rows, cols, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = d_dst.cpu().view(torch.int16).numpy().reshape(-1)
+    s = src.numpy()
+    want = np.empty((rows // 16, cols // 32, 64, 8), dtype=np.int16)
+    for l in range(64):
+        for e in range(8):
+            want[:, :, l, e] = s[(l % 16)::16, :][:, (8 * (l // 16) + e)::32]
+    assert np.array_equal(got, want.reshape(-1))
+
+
+@pytest.mark.parametrize("case", ["b8", "b8_wide", "b1", "b3_ragged"])
+def test_tiny_mfma_packed_weights_bitwise_row_major(case):
+    # The small-batch matrix-core tile reading the tile layout (MK_LOWER_PACKED_WEIGHTS)
+    # does the same products in the same order as with row-major weights: every
+    # activation and the logits are bitwise equal; the packed run also against the oracle.
+    w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, kv_capacity=128,
+                                 name=f"tiny_mfma_{case}", **MFMA_CASES[case])
+    _say(f"tiny MFMA GEMV {case}, packed weights vs row-major")
+    run = MkRun(w)
+    logits = run.step("persistent")
+    acts = run.activations()
+    runp = MkRun(w.replace(packed=1, name=f"tiny_mfma_{case}_packed"), inputs=run.inp)
+    assert runp.graph.mk_graph_kernel_name().startswith("mfma8_")
+    logits_p = runp.step("persistent")
+    acts_p = runp.activations()
+    assert np.array_equal(logits_p, logits), "packed and row-major logits differ"
+    for k in acts:
+        assert np.array_equal(acts_p[k], acts[k]), k
+    assert np.array_equal(runp.step("per_op"), logits_p), "per-op and persistent packed paths differ"
+    ref, inter = _oracle(w, keep=True)
+    compare_activations(w, acts_p, inter, range(w.batch))
+    _check_step(w, logits_p, ref)
+    runp.close()
+    run.close()
+
+
 def test_8b_shapes_2_layers_b32_mfma_all_activations():
     # 8B-class layer shapes (K = 4096 and 14336: 16 and 56 chunks per group; o and down
     # tiles of one 16-row block, gate_up pairs, lm_head groups of 8) with 2 layers,
@@ -310,7 +357,8 @@ def test_8b_shapes_2_layers_b8_mfma_all_activations():
     # gate_up tiles of 6 and 8 interleaved blocks, lm_head groups of 8, 4, 2 and 1),
     # 2 layers, batch 8 with ragged lengths, every activation against the oracle.
     w = workloads.get("8b_b8_ragged").replace(n_layers=2, name="8b_shapes_l2_b8")
-    _say("8B shapes, 2 layers, batch 8 ragged, small-batch MFMA GEMV, all activations")
+    assert w.packed  # the benchmarked layout: matrices in 16-row tiles
+    _say("8B shapes, 2 layers, batch 8 ragged, small-batch MFMA GEMV (packed weights), all activations")
     run = MkRun(w)
     assert run.graph.mk_graph_kernel_name() == "mfma8_bf16_bf16"
     logits = run.step("persistent")
