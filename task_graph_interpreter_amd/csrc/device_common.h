@@ -14,6 +14,7 @@ namespace mk {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // an MFMA bf16 operand
 
 constexpr int kThreads = 512;  // 8 wave64s per workgroup, one workgroup per CU
 constexpr int kWaves = kThreads / 64;

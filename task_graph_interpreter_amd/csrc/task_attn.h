@@ -101,6 +101,90 @@ __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
   }
 }
 
+// Merge the running (m, l, o) states of the workgroup's lane groups for one pass of
+// query heads (log-sum-exp rule) and write the pass's output slots.  State st =
+// wave * kpw + (lane / (64 / kpw)) holds o[h][0 .. VEC) at dims (lane % (64 / kpw)) VEC
+// and (m[h], l[h]); every lane of a state holds the same m and l.
+template <int HM, int VEC>
+__device__ __forceinline__ void partial_merge(const LaunchArgs& a, Smem& sm, bool first, int hc, int hd, int kpw,
+                                              const float (&m)[HM], const float (&l)[HM], const float (&o)[HM][8],
+                                              float* out, size_t out0, int stride) {
+  const int lane = lane_id(), wave = wave_id();
+  const int lpk = 64 / kpw, kl = lane / lpk, dl = lane % lpk;
+  // Merge the running states of every lane group of the workgroup in one LDS pass
+  // (log-sum-exp rule): each group writes its (m, l) and its slice of o, one wave per
+  // head turns the S = kWaves * kpw maxima into the head's M and per-state weights
+  // w_s = e^(m_s - M) (and L = sum_s w_s l_s) with wave reductions, and each thread
+  // then sums one output element over the S states.  Layout in the staging area:
+  // o as [S][HM][hd], then (m, l) as [S][HM][2], then w as [HM][S].
+  const int S = kWaves * kpw;
+  float* po = sm.xs;
+  float* pml = po + (size_t)S * HM * hd;
+  float* pw = pml + (size_t)S * HM * 2;
+  if (!first) __syncthreads();  // the previous pass may still read po / pml / pw
+  {
+    const int st = wave * kpw + kl;
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      if (h < hc) {
+        float* dst = po + ((size_t)st * HM + h) * hd + dl * VEC;
+        *(f32x4*)dst = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+        if (VEC == 8) *(f32x4*)(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+        if (dl == 0) {
+          pml[(st * HM + h) * 2] = m[h];
+          pml[(st * HM + h) * 2 + 1] = l[h];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < hc) {
+    const int h = wave;
+    float mx = -INFINITY;
+    for (int st = lane; st < S; st += 64) mx = fmaxf(mx, pml[(st * HM + h) * 2]);
+    mx = fmaxf(mx, lane_xor<32>(mx));
+    mx = fmaxf(mx, lane_xor<16>(mx));
+    mx = fmaxf(mx, lane_xor<8>(mx));
+    mx = fmaxf(mx, lane_xor<4>(mx));
+    mx = fmaxf(mx, lane_xor<2>(mx));
+    mx = fmaxf(mx, lane_xor<1>(mx));
+    float lsum = 0.f;
+    for (int st = lane; st < S; st += 64) {
+      const float ms = pml[(st * HM + h) * 2];
+      const float w = ms == -INFINITY ? 0.f : __expf(ms - mx);  // every state empty: M = -inf, all 0
+      pw[h * S + st] = w;
+      lsum = fmaf(w, pml[(st * HM + h) * 2 + 1], lsum);
+    }
+    lsum = wave_sum(lsum);
+    if (lane == 0) {
+      st_dev<float>(out, out0 + h * stride + hd, mx);
+      st_dev<float>(out, out0 + h * stride + hd + 1, lsum);
+    }
+  }
+  __syncthreads();
+  trace_mark(a, sm, 1);
+  for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
+    const int h = e / hd, dd = e % hd;
+    const float* wh = pw + h * S;
+    const float* oh = po + (size_t)h * hd + dd;
+    // Blocks of 8 states: the LDS reads of a block are issued together.
+    float acc = 0.f;
+    int st = 0;
+    for (; st + 8 <= S; st += 8) {
+      float ov[8], wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ov[u] = oh[(size_t)(st + u) * HM * hd];
+        wv[u] = wh[st + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(ov[u], wv[u], acc);
+    }
+    for (; st < S; ++st) acc = fmaf(oh[(size_t)st * HM * hd], wh[st], acc);
+    st_dev<float>(out, out0 + h * stride + dd, acc);
+  }
+}
+
 // One pass over the chunk for query heads [hg, hg + HM) of the group; the first pass
 // (hg == 0) prefetches before waiting on the producers.
 template <bool BF16, int HM, int LPK, int R, bool BATCHED>
@@ -315,79 +399,241 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
   }
   if (has_new && wave == 0) fold(knew, vnew, kl == 0);
   trace_mark(a, sm, 0);
-  // Merge the running states of every lane group of the workgroup in one LDS pass
-  // (log-sum-exp rule): each group writes its (m, l) and its slice of o, one wave per
-  // head turns the S = kWaves * kpw maxima into the head's M and per-state weights
-  // w_s = e^(m_s - M) (and L = sum_s w_s l_s) with wave reductions, and each thread
-  // then sums one output element over the S states.  Layout in the staging area:
-  // o as [S][HM][hd], then (m, l) as [S][HM][2], then w as [HM][S].
-  const int S = kWaves * kpw;
-  float* po = sm.xs;
-  float* pml = po + (size_t)S * HM * hd;
-  float* pw = pml + (size_t)S * HM * 2;
-  if (!first) __syncthreads();  // the previous pass may still read po / pml / pw
-  {
-    const int st = wave * kpw + kl;
+  partial_merge<HM, VEC>(a, sm, first, hc, hd, kpw, m, l, o, out, out0, stride);
+  return true;
+}
+
+// The same ATTENTION_PARTIAL pass with the scores on the matrix cores, for a bf16
+// cache with head_dim HD = 64 or 128 (the 16-lane fold above spends most of its
+// time in per-row softmax work that every lane of a row group repeats).
+//  * The chunk's keys go in blocks of 16, dealt to the waves round robin (block
+//    wave + 8 i).  Scores S[key][head] = K[key] . q_head / sqrt(HD) come from
+//    v_mfma_f32_16x16x32_bf16 with A = 16 key rows x 32 dims (lane l: key l % 16,
+//    dims 8 (l / 16) .. +8 of each 32) and B = the pass's query heads as columns
+//    0..3 (columns 4..15 zero); the query is split into bf16 hi and lo parts (q =
+//    hi + lo to about 16 bits) and both products accumulate into the same scores.
+//  * In the result a lane holds 4 keys of one head (column), so the block maximum,
+//    e^(s - m) and the running sum are computed once per (key, head): the maximum
+//    over the block and the rescale factor are shared across the wave with lane
+//    swaps and lane reads.
+//  * p = e^(s - m) goes through a 256-byte slice of LDS private to the wave to the
+//    lanes that hold the matching V rows (row groups of HD / 8 lanes, 16 bytes each,
+//    as in the pass above), which accumulate o[head][dims] += p v.  Those lanes'
+//    (m, l, o) are the states the merge combines (l counted once per wave).
+//  * A ring of NS blocks of K and V is held in registers, loaded before the
+//    dependency wait and refilled in place after each block is folded.  The new
+//    token's row is masked in the ring (it is stale until APPEND has run); wave 0
+//    reads it with device-scope loads after the wait and folds it first, as a block
+//    holding only that row.
+template <int HD, int NS>
+__device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm,
+                                                  int hg) {
+  constexpr int HM = 4, VEC = 8;
+  constexpr int LPK = HD / 8;       // lanes per V row (16 bytes each)
+  constexpr int KPV = 64 / LPK;     // V rows per wave load
+  constexpr int KS = HD / 32;       // 32-dim steps of a key row
+  constexpr int VJ = 16 / KPV;      // V loads per block of 16 keys
+  constexpr int rowq = HD / 8;      // 16-byte pieces per cache row
+  const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc_all = (int)d.reserved[2];
+  const int c = (int)d.reserved[3], base = (int)d.reserved[4];
+  const int g = d.k, chunk = d.kv_len, nchunks = d.m;
+  const int cap = a.kv_capacity, Hkv = a.n_kv_heads, Hq = a.n_q_heads;
+  const int hc = (hc_all - hg) < HM ? (hc_all - hg) : HM;
+  const float* qrot = (const float*)resolve(a, d.in_buf[0]);
+  const size_t head_off = (((size_t)b * Hkv + g) * cap) * rowq;
+  const char* kc = resolve(a, d.in_buf[1]);
+  const char* vc = resolve(a, d.in_buf[2]);
+  const int stride = HD + 2;
+  float* out = (float*)resolve(a, d.out_buf);
+  const size_t out0 = ((size_t)(base + c) * hc_all + hg) * stride;
+  const int pos = ldg<int32_t>((const void*)a.rt[TAG_POSITIONS], b);
+  const bool bad = pos < 0 || pos >= cap || pos >= nchunks * chunk;
+  int hi = (c + 1) * chunk;
+  hi = hi < pos + 1 ? hi : pos + 1;
+  int lo = c * chunk;
+  lo = lo < hi ? lo : hi;
+  const int n = bad ? 0 : hi - lo;
+  const int jnew = pos - lo;  // the new token's key (if inside this chunk)
+  const bool first = hg == 0;
+
+  const int lane = lane_id(), wave = wave_id();
+  const int qc = lane & 15, g4 = lane >> 4;       // score layout: head column, key group
+  const int kv = lane / LPK, dl = lane % LPK;     // V layout: row in a load, dims dl * 8
+  const int nblk = (n + 15) >> 4;
+  const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;  // blocks of this wave
+  const uint32_t head_bytes = (uint32_t)cap * (uint32_t)rowq * 16u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kc + head_off * 16), (short)0, (int)head_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vc + head_off * 16), (short)0, (int)head_bytes, kRawBufferWord3);
+  // Keys past the chunk get an out-of-range offset: the load reads nothing, returns 0.
+  auto koff = [&](int i, int s) -> uint32_t {
+    const int key = 16 * (wave + kWaves * i) + qc;
+    return key < n ? ((uint32_t)(lo + key) * rowq + 4u * s + (uint32_t)g4) * 16u : 0xFFFFFFF0u;
+  };
+  auto voff = [&](int i, int j) -> uint32_t {
+    const int key = 16 * (wave + kWaves * i) + kv + KPV * j;
+    return key < n ? ((uint32_t)(lo + key) * rowq + (uint32_t)dl) * 16u : 0xFFFFFFF0u;
+  };
+  u32x4 kr[NS][KS], vr[NS][VJ];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int e = 0; e < KS; ++e) kr[s][e] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff(s, e), 0, 0);
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) vr[s][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff(s, j), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (first) {
+    if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
+    if (bad) {
+      if (threadIdx.x == 0) raise_status(a, MK_STATUS_BAD_POSITION | t);
+      return false;
+    }
+  }
+  // B operand: column qc = head qc of the pass (zero past hc and for columns >= HM),
+  // dims 32 e + 8 g4 .. +8, scaled by 1/sqrt(HD) and split into bf16 hi and lo.
+  const float scale = 1.0f / sqrtf((float)HD);
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int e = 0; e < KS; ++e) {
+    float qv[8];
+    if (qc < hc) {
+      const size_t q4 = ((size_t)b * Hq * HD + (size_t)(h0 + hg + qc) * HD + 32 * e + 8 * g4) / 4;
+      const f32x4 q0 = ld_dev_f4(qrot, q4), q1 = ld_dev_f4(qrot, q4 + 1);
+      qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w; qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qv[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = qv[u] * scale;
+      const __bf16 h = (__bf16)v;
+      qh[e][u] = h;
+      ql[e][u] = (__bf16)(v - (float)h);
+    }
+  }
+  // The new token's row (written by this step's APPEND), wave 0 only: K in the
+  // score layout (lanes of key 0), V in the row layout (lanes of row 0).
+  const bool has_new = jnew >= 0 && jnew < n;
+  u32x4 knew[KS], vnew[VJ];
+#pragma unroll
+  for (int e = 0; e < KS; ++e) knew[e] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) vnew[j] = u32x4{0u, 0u, 0u, 0u};
+  if (has_new && wave == 0) {
+    const size_t rn = head_off + (size_t)pos * rowq;
+    if (qc == 0) {
+#pragma unroll
+      for (int e = 0; e < KS; ++e) knew[e] = ld_dev_u4(kc, rn + 4 * e + g4);
+    }
+    if (kv == 0) vnew[0] = ld_dev_u4(vc, rn + dl);
+  }
+  float m = -INFINITY, l = 0.f;  // score layout: head qc; l over this lane's keys
+  float o[HM][8];
+#pragma unroll
+  for (int h = 0; h < HM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  float* pw = sm.red + wave * 64;  // [16 keys][HM] p of the current block
+  // Fold one block: keys key0 + 0..15; `only` >= 0 keeps just that key (the new
+  // row), else keys < n other than the new token's.
+  auto block = [&](const u32x4 (&kb)[KS], const u32x4 (&vb)[VJ], int key0, int only) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < KS; ++e) {
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, kb[e]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[e], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[e], acc, 0, 0, 0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 4 * g4 + r;
+      const bool ok = only >= 0 ? key == only : (key < n && key != jnew);
+      sc[r] = ok ? acc[r] : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, lane_xor<16>(bm));
+    bm = fmaxf(bm, lane_xor<32>(bm));
+    const float mn = fmaxf(m, bm);
+    const float al = (m == mn) ? 1.f : __expf(m - mn);  // m = -inf -> 0
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = sc[r] == -INFINITY ? 0.f : __expf(sc[r] - mn);
+    l = fmaf(l, al, (p[0] + p[1]) + (p[2] + p[3]));
+    m = mn;
+    if (qc < HM) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[(4 * g4 + r) * HM + qc] = p[r];
+    }
+    float alh[HM];
+    bool rescale = false;
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
-      if (h < hc) {
-        float* dst = po + ((size_t)st * HM + h) * hd + dl * VEC;
-        *(f32x4*)dst = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-        if (VEC == 8) *(f32x4*)(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
-        if (dl == 0) {
-          pml[(st * HM + h) * 2] = m[h];
-          pml[(st * HM + h) * 2 + 1] = l[h];
-        }
-      }
+      alh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), h));
+      rescale |= alh[h] != 1.f;
     }
-  }
-  __syncthreads();
-  if (wave < hc) {
-    const int h = wave;
-    float mx = -INFINITY;
-    for (int st = lane; st < S; st += 64) mx = fmaxf(mx, pml[(st * HM + h) * 2]);
-    mx = fmaxf(mx, lane_xor<32>(mx));
-    mx = fmaxf(mx, lane_xor<16>(mx));
-    mx = fmaxf(mx, lane_xor<8>(mx));
-    mx = fmaxf(mx, lane_xor<4>(mx));
-    mx = fmaxf(mx, lane_xor<2>(mx));
-    mx = fmaxf(mx, lane_xor<1>(mx));
-    float lsum = 0.f;
-    for (int st = lane; st < S; st += 64) {
-      const float ms = pml[(st * HM + h) * 2];
-      const float w = ms == -INFINITY ? 0.f : __expf(ms - mx);  // every state empty: M = -inf, all 0
-      pw[h * S + st] = w;
-      lsum = fmaf(w, pml[(st * HM + h) * 2 + 1], lsum);
-    }
-    lsum = wave_sum(lsum);
-    if (lane == 0) {
-      st_dev<float>(out, out0 + h * stride + hd, mx);
-      st_dev<float>(out, out0 + h * stride + hd + 1, lsum);
-    }
-  }
-  __syncthreads();
-  trace_mark(a, sm, 1);
-  for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
-    const int h = e / hd, dd = e % hd;
-    const float* wh = pw + h * S;
-    const float* oh = po + (size_t)h * hd + dd;
-    // Blocks of 8 states: the LDS reads of a block are issued together.
-    float acc = 0.f;
-    int st = 0;
-    for (; st + 8 <= S; st += 8) {
-      float ov[8], wv[8];
+    // The p slice is written and read by this wave only: LDS operations of a wave
+    // complete in order, the wait keeps the compiler from reordering them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (rescale) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        ov[u] = oh[(size_t)(st + u) * HM * hd];
-        wv[u] = wh[st + u];
-      }
+      for (int h = 0; h < HM; ++h)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(ov[u], wv[u], acc);
+        for (int e = 0; e < 8; ++e) o[h][e] *= alh[h];
     }
-    for (; st < S; ++st) acc = fmaf(oh[(size_t)st * HM * hd], wh[st], acc);
-    st_dev<float>(out, out0 + h * stride + dd, acc);
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) {
+      float vf[8];
+      unpack<true>(vb[j], vf);
+      const f32x4 pj = *(const f32x4*)(pw + (kv + KPV * j) * HM);
+      const float ph[HM] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+      for (int h = 0; h < HM; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(ph[h], vf[e], o[h][e]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // The new row first: its registers are then free during the streaming loop (its
+  // loads were issued with the query's, which every block waits for anyway).
+  if (has_new && wave == 0) block(knew, vnew, jnew, jnew);
+  for (int i0 = 0; i0 < nbw; i0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int i = i0 + s;
+      if (i < nbw) block(kr[s], vr[s], 16 * (wave + kWaves * i), -1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < KS; ++e) kr[s][e] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff(i + NS, e), 0, 0);
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) vr[s][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff(i + NS, j), 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  trace_mark(a, sm, 0);
+  // States for the merge: each V row group of the wave is a state; all share the
+  // wave's m, and the wave's l (summed over the score layout's key groups) is counted
+  // in row group 0 only.
+  float lt = l + lane_xor<16>(l);
+  lt += lane_xor<32>(lt);
+  float mh[HM], lh[HM];
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), h));
+    lh[h] = kv == 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), h)) : 0.f;
+  }
+  partial_merge<HM, VEC>(a, sm, first, hc, HD, KPV, mh, lh, o, out, out0, stride);
   return true;
+}
+
+template <int HD, int NS>
+__device__ __forceinline__ void partial_heads_mfma(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  const int hc = (int)d.reserved[2];
+  for (int hg = 0; hg < hc; hg += 4)
+    if (!partial_pass_mfma<HD, NS>(a, d, t, sm, hg)) return;
 }
 
 template <bool KVBF16, int LPK, int R, bool BATCHED>
@@ -399,8 +645,18 @@ __device__ __forceinline__ void partial_heads(const LaunchArgs& a, const mk_task
 
 // Lanes per cache row (head_dim * element size / 16) as a compile-time constant for
 // the common shapes (head_dim 64 and 128), else a run-time value.
-template <bool KVBF16, bool BATCHED>
+// Blocks of 16 keys in flight per wave in the matrix-core pass.
+constexpr int kAttnRing = 2;
+
+// MFMA: the matrix-core pass (kernels for batches above 1, whose chunks are long
+// enough for the fold's VALU work to bound the pass; the batch-1 kernels keep the
+// 16-lane fold, which is as fast on their short chunks).
+template <bool KVBF16, bool BATCHED, bool MFMA>
 __device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  if constexpr (KVBF16 && MFMA) {
+    if (d.n == 128) return partial_heads_mfma<128, kAttnRing>(a, d, t, sm);
+    if (d.n == 64) return partial_heads_mfma<64, kAttnRing>(a, d, t, sm);
+  }
   // R rounds per batch: 2 for chunks of at most two rounds, else 4.
   const int lpk = d.n * (KVBF16 ? 2 : 4) / 16;
   const bool short_chunk = d.kv_len <= 2 * kWaves * (64 / lpk);

@@ -43,8 +43,6 @@
 
 namespace mk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kMfmaKC = 256;                 // k per chunk: 4 compute waves x 2 x 32
 constexpr int kMfmaXPitch = kMfmaKC + 8;     // bf16 per staged row (+16 B against bank conflicts)
 constexpr int kMfmaXHalf = 32 * kMfmaXPitch; // bf16 per staged chunk part (hi or lo; 32 batch rows)

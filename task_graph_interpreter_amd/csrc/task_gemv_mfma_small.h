@@ -16,11 +16,13 @@
 //    the 16-row tile layout (mk_pack_matrix, MK_LOWER_PACKED_WEIGHTS), one contiguous
 //    kilobyte, which streams about a fifth faster from HBM;
 //  * B = 32 k x 16 columns: columns 0..7 hold the bf16 "hi" parts of the 8 batch rows'
-//    input, columns 8..15 their "lo" parts (u = x gamma = hi + lo, hi = bf16(u),
-//    lo = bf16(u - hi): the input keeps about 16 significant bits), so ONE product
-//    per block and k-step gives W hi and W lo side by side; lane l builds column l % 16
-//    for k = 8 (l / 16) .. +8.  Lanes l and l ^ 8 need the same 8 input values: each
-//    loads 4 of them (16 bytes) and takes the other 4 from its partner with a DPP move;
+//    input, columns 8..15 their "lo" parts (u = x gamma = hi + lo, hi = u with the low
+//    16 bits cleared, lo = the same of the exact remainder u - hi: the input keeps
+//    about 16 significant bits), so ONE product per block and k-step gives W hi and W lo
+//    side by side; lane l builds column l % 16 for k = 8 (l / 16) .. +8.  Lanes l and
+//    l ^ 8 (hi and lo of one batch row) each load and split 4 of the 8 input values
+//    and swap the halves the other needs with one DPP move per bf16 pair -- this
+//    operand build is the tile's VALU cost per k-step (about 40 instructions);
 //  * D: lane l holds column l % 16 of rows 4 (l / 16) .. +4;  y[b, row] sums columns
 //    b and b + 8.
 //
@@ -40,7 +42,6 @@
 
 namespace mk {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Byte offset of lane `lane`'s 16 weight bytes of block gb at the wave's k-step s, which
 // covers k = 32 (w + 8 s) .. +32 (kPastEnd past the last step: reads nothing).  Either
@@ -75,12 +76,15 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
                                    : 2u * g.K * (uint32_t)colj + 16u * (uint32_t)kq + 64u * (uint32_t)w;
   const uint32_t sstride = a.wpacked ? 8192u : 512u;
   const bool lo_lane = colj >= 8;
-  // Input: this lane's 4 of the 8 values of batch row bb at k = k0 + 32 s + 8 kq
-  // (+4 on the "lo" lanes); rows past the batch read nothing (zeros).
+  // Input: this lane's 4 of the 8 values of batch row bb at k = k0 + 256 s + 8 kq (+4 on
+  // the lo lanes), one 16-byte load, and the 4 matching gamma values (8 bytes); rows
+  // past the batch read nothing (zeros).
   const uint32_t xbase = (uint32_t)bb * g.K * 4u + (uint32_t)(k0 + 8 * kq + (lo_lane ? 4 : 0)) * 4u;
   auto xoff = [&](int s) -> uint32_t { return (s < nst && bb < B) ? xbase + (uint32_t)s * 1024u : kPastEnd; };
-  const uint32_t gbase = (uint32_t)(k0 + 8 * kq) * 2u;
+  const uint32_t gbase = (uint32_t)(k0 + 8 * kq + (lo_lane ? 4 : 0)) * 2u;
   auto goff = [&](int s) -> uint32_t { return s < nst ? gbase + (uint32_t)s * 512u : kPastEnd; };
+  // Without the norm the gamma loads return zeros: OR-ing in bf16 1.0 makes u = x.
+  const uint32_t gor = norm ? 0u : 0x3F803F80u;
 
   // The ring is filled in the order the loop consumes and refills it (each slot's
   // loads kept together by a scheduling barrier): the wait counts the compiler places
@@ -100,11 +104,12 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
     if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __syncthreads();
   }
-  u32x4 xr[D], gr[D];
+  u32x4 xr[D];
+  u32x2 gr[D];
 #pragma unroll
   for (int dd = 0; dd < D; ++dd) {
     xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(dd), 0, 0);
-    gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(dd), 0, 0);
+    gr[dd] = __builtin_amdgcn_raw_buffer_load_b64(grs, goff(dd), 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   f32x4 acc[G];
@@ -114,43 +119,50 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   // One k-step from ring slot dd (steps s0 + dd; the slot is refilled with s0 + dd + D).
   auto step = [&](int dd, int s0) __attribute__((always_inline)) {
     const int sn = s0 + dd + D;
-    // Assemble the 8 input values of this lane's column: its own 4 and its partner's
-    // (lane ^ 8).
-    float xv[8];
+    // u = x gamma for this lane's 4 values (the sum of squares is of x itself).
+    float u[4];
     {
-      const u32x4 mine = xr[dd];
-      const float m0 = __uint_as_float(mine.x), m1 = __uint_as_float(mine.y);
-      const float m2 = __uint_as_float(mine.z), m3 = __uint_as_float(mine.w);
-      const float p0 = lane_xor<8>(m0), p1 = lane_xor<8>(m1), p2 = lane_xor<8>(m2), p3 = lane_xor<8>(m3);
-      xv[0] = lo_lane ? p0 : m0; xv[1] = lo_lane ? p1 : m1; xv[2] = lo_lane ? p2 : m2; xv[3] = lo_lane ? p3 : m3;
-      xv[4] = lo_lane ? m0 : p0; xv[5] = lo_lane ? m1 : p1; xv[6] = lo_lane ? m2 : p2; xv[7] = lo_lane ? m3 : p3;
-    }
-    float gv[8];
-    {
-      const u32x4 gg = gr[dd];
-      gv[0] = bf16_lo(gg.x); gv[1] = bf16_hi(gg.x); gv[2] = bf16_lo(gg.y); gv[3] = bf16_hi(gg.y);
-      gv[4] = bf16_lo(gg.z); gv[5] = bf16_hi(gg.z); gv[6] = bf16_lo(gg.w); gv[7] = bf16_hi(gg.w);
+      const u32x4 xx = xr[dd];
+      const u32x2 gg = gr[dd];
+      const float xv[4] = {__uint_as_float(xx.x), __uint_as_float(xx.y), __uint_as_float(xx.z),
+                           __uint_as_float(xx.w)};
+      const uint32_t g0 = gg.x | gor, g1 = gg.y | gor;
+      const float gv[4] = {bf16_lo(g0), bf16_hi(g0), bf16_lo(g1), bf16_hi(g1)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss = fmaf(xv[e], xv[e], ss);
+        u[e] = xv[e] * gv[e];
+      }
     }
     // Every read of the slots' old values is done before they are refilled, so the
     // refills land in the same registers (no copies, whose waits would drain the ring):
-    // the unpacked values are pinned in registers first.
+    // the products are pinned in registers first.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(xv[e]), "+v"(gv[e]));
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(u[e]));
     __builtin_amdgcn_sched_barrier(0);
     xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
-    gr[dd] = __builtin_amdgcn_raw_buffer_load_b128(grs, goff(sn), 0, 0);
-    uint32_t bw[4];
+    gr[dd] = __builtin_amdgcn_raw_buffer_load_b64(grs, goff(sn), 0, 0);
+    // hi = u with the low 16 bits cleared, lo = the same of the exact remainder u - hi;
+    // v_perm packs the upper halves of two floats into one bf16 pair.  The lane splits
+    // its own 4 values and swaps half with its partner (lane ^ 8): a hi lane keeps the
+    // hi parts of k .. k+3 and receives those of k+4 .. k+7, a lo lane the reverse.
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float u0 = norm ? xv[2 * e] * gv[2 * e] : xv[2 * e];
-      const float u1 = norm ? xv[2 * e + 1] * gv[2 * e + 1] : xv[2 * e + 1];
-      ss = fmaf(xv[2 * e], xv[2 * e], fmaf(xv[2 * e + 1], xv[2 * e + 1], ss));
-      // hi = bf16(u) (round to nearest even), lo = bf16(u - hi)
-      const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)u0, (__bf16)u1});
-      const float r0 = u0 - __uint_as_float(h << 16), r1 = u1 - __uint_as_float(h & 0xFFFF0000u);
-      const uint32_t l = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)r0, (__bf16)r1});
-      bw[e] = lo_lane ? l : h;
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t a0 = __float_as_uint(u[2 * e]), a1 = __float_as_uint(u[2 * e + 1]);
+      hw[e] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+      const float r0 = u[2 * e] - __uint_as_float(a0 & 0xFFFF0000u);
+      const float r1 = u[2 * e + 1] - __uint_as_float(a1 & 0xFFFF0000u);
+      lw[e] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
     }
+    const uint32_t s0w = lo_lane ? hw[0] : lw[0], s1w = lo_lane ? hw[1] : lw[1];
+    const uint32_t r0w = __float_as_uint(lane_xor<8>(__uint_as_float(s0w)));
+    const uint32_t r1w = __float_as_uint(lane_xor<8>(__uint_as_float(s1w)));
+    uint32_t bw[4];
+    bw[0] = lo_lane ? r0w : hw[0];
+    bw[1] = lo_lane ? r1w : hw[1];
+    bw[2] = lo_lane ? lw[0] : r0w;
+    bw[3] = lo_lane ? lw[1] : r1w;
     const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
 #pragma unroll
     for (int r = 0; r < G; ++r) {
@@ -172,12 +184,12 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
 #pragma unroll
     for (int dd = 0; dd < D; ++dd) step(dd, s0);
   }
-  // Sum of squares of each batch row over this wave's segment: the "hi" lanes (columns
-  // 0..7) of the four k-quarters hold every value once.
+  // Sum of squares of each batch row over this wave's segment: the hi and lo lanes of
+  // the row's column pair in the four k-quarters hold every value once.
   float* part = sm.xs;                       // [kWaves][G][64 lanes] f32x4
   float* row_ss = sm.red + kRedFloats - 128;  // [kWaves][8]
   if (need_ss) {
-    ss = lo_lane ? 0.f : ss;
+    ss += lane_xor<8>(ss);  // the hi and lo lanes of a row hold its two halves
     ss += lane_xor<16>(ss);
     ss += lane_xor<32>(ss);
     if (lane < 8) row_ss[w * 8 + lane] = ss;
