@@ -18,7 +18,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // an MFMA bf16 oper
 
 constexpr int kThreads = 512;  // 8 wave64s per workgroup, one workgroup per CU
 constexpr int kWaves = kThreads / 64;
-// LDS: x staging, GEMV weight prefetch, attention merge.  Most of the CU's 160 KB, so
+// LDS: x staging, GEMV partial sums, attention merge.  Most of the CU's 160 KB, so
 // the persistent kernel gets exactly one workgroup per CU (co-residency of the whole
 // grid).
 constexpr int kSmemBytes = 148 * 1024;
@@ -27,6 +27,10 @@ constexpr int kRedFloats = 1024;  // reduction scratch
 // Arrival counters sit one per 128-byte line, so the atomics of a join's fan-out (one
 // wave incrementing up to 256 children) and the children's polls never share a line.
 constexpr uint32_t kArrivalStride = 32;
+// A NOP join's arrivals are spread over this many counters (parent task index modulo
+// the count picks one), each on its own line: a join with 256 parents then takes 32
+// increments per word instead of 256 on one, and its children poll all of them.
+constexpr uint32_t kJoinShards = 8;
 // Word 3 of a raw (stride 0, untyped) buffer resource on gfx950, and the cache-policy
 // operand of a buffer load that streams (non-temporal).
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -62,7 +66,9 @@ struct Smem {
 struct LaunchArgs {
   const mk_task_t* tasks;
   const uint32_t* edges;      // dependents array (CSR, as lowered)
-  const uint32_t* join;       // per task: its NOP join parent, or 0xFFFFFFFF
+  const uint32_t* eslot;      // per edge: the arrival counter it increments (a join's shard)
+  const uint32_t* join;       // per task: first counter of its NOP join's shards, or 0xFFFFFFFF
+  const uint32_t* jcnt;       // per join shard (counter index - n_tasks): parents counting on it
   const uint32_t* order;      // static schedule: task lists grouped by workgroup
   const uint32_t* order_off;  // [grid + 1]; null = dynamic tickets
   const uint64_t* table;
@@ -306,19 +312,47 @@ __device__ __forceinline__ uint32_t poll_counter(const LaunchArgs& a, uint32_t t
   }
 }
 
+// Poll until every shard of a NOP join has its parents of this step: shard s of the
+// join whose counters start at `base` expects epoch * jcnt[base - n_tasks + s].  The
+// shards are read together each round.  One thread; 0 if the step was abandoned.
+__device__ __forceinline__ uint32_t poll_join(const LaunchArgs& a, uint32_t t, uint32_t base) {
+  uint32_t target[kJoinShards];
+#pragma unroll
+  for (uint32_t s = 0; s < kJoinShards; ++s) target[s] = a.epoch * ldg<uint32_t>(a.jcnt, base - a.n_tasks + s);
+  const uint64_t t0 = clock100();
+  for (uint32_t it = 1;; ++it) {
+    uint32_t v[kJoinShards];
+#pragma unroll
+    for (uint32_t s = 0; s < kJoinShards; ++s)
+      v[s] = __hip_atomic_load((MK_GLOBAL uint32_t*)(a.arrivals + (size_t)(base + s) * kArrivalStride),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+#pragma unroll
+    for (uint32_t s = 0; s < kJoinShards; ++s) ok &= (int32_t)(v[s] - target[s]) >= 0;
+    if (ok) return 1;
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 15u) == 0u) {
+      if (clock100() - t0 > a.wait_limit) {
+        raise_status(a, MK_STATUS_TIMEOUT | t);
+        return 0;
+      }
+      if (read_status(a) != 0) return 0;
+    }
+  }
+}
+
 // Poll until all of this step's parents of task t have arrived.  A task whose parents
-// include a NOP join (at most one: one join per op) waits for the join's own counter
-// to reach epoch * indeg(join) -- the join's parents count on it directly, nobody
-// fires it -- and for its own counter to reach epoch * (indeg - 1); any other task
-// waits for epoch * indeg on its own counter.  One thread; returns 0 if the step was
-// abandoned (timeout, or another workgroup raised an error).
+// include a NOP join (at most one: one join per op) waits for the join's shards (the
+// join's parents count on them directly, nobody fires the join) and for its own
+// counter to reach epoch * (indeg - 1); any other task waits for epoch * indeg on its
+// own counter.  One thread; returns 0 if the step was abandoned (timeout, or another
+// workgroup raised an error).
 __device__ __forceinline__ uint32_t poll_deps(const LaunchArgs& a, uint32_t t, int32_t indeg) {
   if (indeg == 0) return 1;
   const uint32_t j = ldg<uint32_t>(a.join, t);
   uint32_t ok = 1, own = (uint32_t)indeg;
   if (j != 0xFFFFFFFFu) {
-    const uint32_t jdeg = ldg<uint32_t>(a.tasks, (size_t)j * 16 + 2);  // remaining_deps
-    ok = poll_counter(a, t, a.arrivals + (size_t)j * kArrivalStride, a.epoch * jdeg);
+    ok = poll_join(a, t, j);
     own -= 1;
   }
   if (ok && own > 0) ok = poll_counter(a, t, a.arrivals + (size_t)t * kArrivalStride, a.epoch * own);
@@ -344,12 +378,13 @@ __device__ __forceinline__ bool dep_wait(const LaunchArgs& a, uint32_t t, int32_
   return sm.flag != 0;
 }
 
-// Count one arrival on each of the n dependents listed at edges[off] (a NOP join
-// counts like any task; its children poll its counter).  Wave 0 only; the caller has
-// waited for its own data stores to be acknowledged.
+// Count one arrival on each of the n dependents listed at edges[off]: on the
+// dependent's own counter, or for a NOP join on the join shard this parent feeds
+// (eslot holds the counter of every edge).  Wave 0 only; the caller has waited for its
+// own data stores to be acknowledged.
 __device__ __forceinline__ void signal_dependents(const LaunchArgs& a, uint32_t off, uint32_t n) {
   for (uint32_t i = lane_id(); i < n; i += 64) {
-    const uint32_t c = ldg<uint32_t>(a.edges, off + i);
+    const uint32_t c = ldg<uint32_t>(a.eslot, off + i);
     __hip_atomic_fetch_add((MK_GLOBAL uint32_t*)a.arrivals + (size_t)c * kArrivalStride, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -35,19 +35,19 @@ struct Spec {
 constexpr bool kb_compiled(int KB) { return KB == 1 || KB == 2 || KB == 4 || KB == 8 || KB == 16 || KB == 28; }
 
 template <int BM, bool BF16, int KB>
-__device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
-  if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm, pre);
-  else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm, pre);
-  else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm, pre);
-  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm, pre);
-  else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm, pre);
-  else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm, pre);
-  else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm, pre);
-  else gemv_run<BM, BF16, 0, 1, 1>(a, d, t, sm, false);
+__device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
+  if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm);
+  else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm);
+  else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm);
+  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm);
+  else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm);
+  else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm);
+  else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm);
+  else gemv_run<BM, BF16, 0, 1, 1>(a, d, t, sm);
 }
 
 template <class S>
-__device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
+__device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   if constexpr (S::BM == 32) {  // batched tiles on the matrix cores (every GEMV of the graph)
     gemv_mfma(a, d, t, sm);
     return;
@@ -57,53 +57,16 @@ __device__ __forceinline__ void gemv_spec(const LaunchArgs& a, const mk_task_t& 
   }
   constexpr int VEC = S::WBF16 ? 8 : 4;
   const int kb = (d.k / VEC + 63) >> 6;
-  if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm, pre);
-  else if (S::KBD > 0 && S::KBD != S::KBA && kb == S::KBD) gemv_kb<S::BM, S::WBF16, S::KBD>(a, d, t, sm, pre);
-  else gemv_run<S::BM, S::WBF16, 0, 1, 1>(a, d, t, sm, false);
+  if (S::KBA > 0 && kb == S::KBA) gemv_kb<S::BM, S::WBF16, S::KBA>(a, d, t, sm);
+  else if (S::KBD > 0 && S::KBD != S::KBA && kb == S::KBD) gemv_kb<S::BM, S::WBF16, S::KBD>(a, d, t, sm);
+  else gemv_run<S::BM, S::WBF16, 0, 1, 1>(a, d, t, sm);
 }
 
-// Issue the LDS prefetch of the workgroup's next task dn (a GEMV tile on the
-// compile-time streaming path) while the current task, which uses at most lds_used
-// bytes at the start of the LDS, is still waiting or running.  Returns whether the
-// prefetch was issued (the tile then skips its own).
+// Run task t.
 template <class S>
-__device__ __forceinline__ bool gemv_spec_prefetch(const LaunchArgs& a, const mk_task_t& dn, int lds_used, Smem& sm) {
-  if constexpr (S::BM == 32 || S::BM == 16) {
-    return false;
-  } else {
-    if (dn.op_id != MK_OP_GEMV) return false;
-    constexpr int VEC = S::WBF16 ? 8 : 4;
-    const int kb = (dn.k / VEC + 63) >> 6;
-    if constexpr (S::KBA > 0 && kb_compiled(S::KBA))
-      if (kb == S::KBA) return gemv_prefetch_ahead<S::BM, S::WBF16, S::KBA>(a, dn, lds_used, sm);
-    if constexpr (S::KBD > 0 && S::KBD != S::KBA && kb_compiled(S::KBD))
-      if (kb == S::KBD) return gemv_prefetch_ahead<S::BM, S::WBF16, S::KBD>(a, dn, lds_used, sm);
-    return false;
-  }
-}
-
-// Bytes at the start of the LDS used by a task under which the next GEMV tile's LDS
-// prefetch is issued early (-1: none).  Only the combine qualifies: it waits for
-// every partial of its group and touches no LDS, while APPEND and the partials sit on
-// the critical path, where a bulk prefetch issued first would delay their own loads
-// (a wave's loads complete in issue order).
-__device__ __forceinline__ int prefetch_host_lds_bytes(const mk_task_t& d) {
-  return d.op_id == MK_OP_ATTENTION_COMBINE ? 0 : -1;
-}
-
-// Run task t.  pre: its LDS prefetch was issued by the previous task.  dn (may be
-// null): the workgroup's next task; a combine issues dn's LDS prefetch first when dn
-// is a GEMV tile on the streaming path.  Returns whether that prefetch was issued.
-template <class S>
-__device__ __forceinline__ bool run_task_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre,
-                                              const mk_task_t* dn) {
-  bool ahead = false;
-  if (dn != nullptr) {
-    const int used = prefetch_host_lds_bytes(d);
-    if (used >= 0) ahead = gemv_spec_prefetch<S>(a, *dn, used, sm);
-  }
+__device__ __forceinline__ void run_task_spec(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   switch (d.op_id) {
-    case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm, pre); break;
+    case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm); break;
     case MK_OP_ATTENTION_APPEND: task_append(a, d, t, sm); break;
     case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16, S::BM == 32, (S::BM > 1)>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
@@ -112,7 +75,6 @@ __device__ __forceinline__ bool run_task_spec(const LaunchArgs& a, const mk_task
     case MK_OP_SAMPLE: task_sample(a, d, t, sm); break;
     default: break;  // NOP joins never run as tasks: their children poll their counter
   }
-  return ahead;
 }
 
 __device__ __forceinline__ uint32_t claim_ticket(const LaunchArgs& a) {
@@ -153,8 +115,7 @@ __device__ __forceinline__ uint32_t next_task(const LaunchArgs& a, uint32_t& pos
 // The persistent interpreter.  Tasks are fetched two ahead: while task i runs, the
 // descriptors of tasks i and i + 1 are in LDS and the id of task i + 2 is being
 // fetched (the claim's round trip, or the list read, and the descriptor fetch overlap
-// the current task), and an attention task can start the next GEMV tile's LDS
-// prefetch.  Descriptors and ids rotate through three LDS slots, which is safe because
+// the current task).  Descriptors and ids rotate through three LDS slots, which is safe because
 // every iteration ends in a workgroup barrier and slot i + 2 is written only at the
 // end of iteration i.  In dynamic mode each workgroup makes exactly one failing claim
 // per step, so the ticket counter advances by n_tasks + grid per step and never needs
@@ -181,15 +142,12 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
     if (t1 < a.n_tasks) stage_desc(a, t1, sm, 1);
   }
   __syncthreads();
-  bool pre = false;  // this task's LDS prefetch was issued by the previous task
   for (int s = 0;; s = s == 2 ? 0 : s + 1) {
     const int s1 = s == 2 ? 0 : s + 1, s2 = s1 == 2 ? 0 : s1 + 1;
     const uint32_t t = __builtin_amdgcn_readfirstlane(sm.ticket[s]);
     if (t >= a.n_tasks || __builtin_amdgcn_readfirstlane(sm.stop) != 0) break;
     const mk_task_t d = read_desc(sm, s);
     const uint32_t tn = __builtin_amdgcn_readfirstlane(sm.ticket[s1]);
-    mk_task_t dn;
-    if (tn < a.n_tasks) dn = read_desc(sm, s1);
     uint64_t t_claim = 0;
     uint32_t nn = 0xFFFFFFFFu, status = 0;
     if (threadIdx.x == 0) {
@@ -202,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
       // release, which waits for all of the workgroup's outstanding memory operations.
       status = read_status(a);
     }
-    pre = run_task_spec<S>(a, d, t, sm, pre, tn < a.n_tasks ? &dn : nullptr);
+    run_task_spec<S>(a, d, t, sm);
     uint64_t t_end = 0;
     if (threadIdx.x == 0) {
       if (trace) t_end = clock100();
@@ -235,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void per_op_kernel(LaunchArgs a) {
   __syncthreads();
   mk_task_t d = read_desc(sm, 0);
   d.remaining_deps = 0;
-  run_task_spec<S>(a, d, t, sm, false, nullptr);
+  run_task_spec<S>(a, d, t, sm);
 }
 
 // Level-synchronous variant ("Mega kernel initial", 1y33.com, the level section: the
@@ -264,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void level_kernel(LaunchArgs a) {
       __syncthreads();
       mk_task_t d = read_desc(sm, 0);
       d.remaining_deps = 0;
-      run_task_spec<S>(a, d, t, sm, false, nullptr);
+      run_task_spec<S>(a, d, t, sm);
       // Every wave's loads (LDS copies included) have landed and every wave is done
       // with the LDS before the next descriptor is staged.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -155,7 +155,10 @@ struct mk_graph {
   char* d_blob = nullptr;
   mk_task_t* d_tasks = nullptr;
   uint32_t* d_edges = nullptr;       // as lowered
-  uint32_t* d_join = nullptr;        // per task: its NOP join parent, or 0xFFFFFFFF
+  uint32_t* d_eslot = nullptr;       // per edge: the arrival counter it increments
+  uint32_t* d_join = nullptr;        // per task: its NOP join's first shard counter, or 0xFFFFFFFF
+  uint32_t* d_jcnt = nullptr;        // per join shard: parents counting on it
+  uint32_t n_counters = 0;           // tasks + joins x kJoinShards
   uint32_t* d_order = nullptr;       // static schedule lists
   uint32_t* d_order_off = nullptr;   // [grid + 1]
   uint32_t* d_lvl = nullptr;         // level-synchronous lists: non-NOP tasks by level
@@ -212,7 +215,9 @@ mk::LaunchArgs make_args(const mk_graph* g, const int32_t* tokens, const int32_t
   std::memset(&a, 0, sizeof(a));
   a.tasks = g->d_tasks;
   a.edges = g->d_edges;
+  a.eslot = g->d_eslot;
   a.join = g->d_join;
+  a.jcnt = g->d_jcnt;
   if (g->sched_mode == MK_SCHED_STATIC) {
     a.order = g->d_order;
     a.order_off = g->d_order_off;
@@ -273,7 +278,7 @@ int check_workspace(const mk_graph* g) {
 }
 
 int reset_state(mk_graph* g, hipStream_t s) {
-  const uint32_t n = (uint32_t)g->low.tasks.size();
+  const uint32_t n = g->n_counters;
   const uint32_t blocks = (n + 255) / 256 > 0 ? (n + 255) / 256 : 1;
   hipLaunchKernelGGL(mk::reset_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0, s, g->d_arrivals, n,
                      g->d_ctrl);
@@ -420,24 +425,44 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   }
   const mk::Schedule& S = g->sched;
 
-  // One blob: 64-byte header, task array, edge array as lowered, each task's NOP join
-  // parent (a task has at most one: the lowering emits one join per op), the static
-  // lists and their offsets.
+  // One blob: 64-byte header, task array, edge array as lowered, the counter each edge
+  // increments, each task's NOP join (a task has at most one: the lowering emits one
+  // join per op) as the first of the join's shard counters, the parents per shard, the
+  // static lists and their offsets.  Counters: one per task, then kJoinShards per join;
+  // parent p of a join counts on the join's shard p % kJoinShards.
   const size_t nt = L.tasks.size(), ne = L.edges.size(), no = S.order.size();
-  std::vector<uint32_t> join(nt, 0xFFFFFFFFu);
-  for (size_t n = 0; n < nt; ++n) {
-    const mk_task_t& d = L.tasks[n];
+  constexpr uint32_t JS = mk::kJoinShards;
+  std::vector<uint32_t> jord(nt, 0xFFFFFFFFu);
+  uint32_t nj = 0;
+  for (size_t n = 0; n < nt; ++n)
+    if (L.tasks[n].op_id == MK_OP_NOP) jord[n] = nj++;
+  std::vector<uint32_t> join(nt, 0xFFFFFFFFu), eslot(ne), jcnt((size_t)nj * JS, 0u);
+  for (size_t p = 0; p < nt; ++p) {
+    const mk_task_t& d = L.tasks[p];
+    for (int32_t i = 0; i < d.num_dependents; ++i) {
+      const size_t k = (size_t)d.dependents_offset + i;
+      const uint32_t c = L.edges[k];
+      if (jord[c] == 0xFFFFFFFFu) {
+        eslot[k] = c;
+      } else {
+        eslot[k] = (uint32_t)nt + jord[c] * JS + (uint32_t)(p % JS);
+        ++jcnt[(size_t)jord[c] * JS + p % JS];
+      }
+    }
     if (d.op_id != MK_OP_NOP) continue;
     for (int32_t i = 0; i < d.num_dependents; ++i) {
       const uint32_t c = L.edges[(size_t)d.dependents_offset + i];
       if (join[c] != 0xFFFFFFFFu) return fail(mk::set_error(MK_ERR_INVALID, "a task with two join parents"));
-      join[c] = (uint32_t)n;
+      join[c] = (uint32_t)nt + jord[p] * JS;
     }
   }
+  g->n_counters = (uint32_t)nt + nj * JS;
   const size_t off_tasks = sizeof(mk::BlobHeader);
   const size_t off_edges = off_tasks + nt * sizeof(mk_task_t);
-  const size_t off_join = off_edges + ne * 4;
-  const size_t off_order = off_join + nt * 4;
+  const size_t off_eslot = off_edges + ne * 4;
+  const size_t off_join = off_eslot + ne * 4;
+  const size_t off_jcnt = off_join + nt * 4;
+  const size_t off_order = off_jcnt + jcnt.size() * 4;
   const size_t off_order_off = off_order + no * 4;
   // RoPE coefficients of every cache slot: the angle pos * theta^(-2i/hd) and its
   // cosine and sine in binary64, rounded to binary32.  They depend on the position
@@ -467,19 +492,24 @@ int mk_build_graph(const mk_model_cfg* cfg, const mk_weights* weights, void* scr
   std::memcpy(blob.data(), &L.header, sizeof(mk::BlobHeader));
   std::memcpy(blob.data() + off_tasks, L.tasks.data(), nt * sizeof(mk_task_t));
   if (ne) std::memcpy(blob.data() + off_edges, L.edges.data(), ne * 4);
+  if (ne) std::memcpy(blob.data() + off_eslot, eslot.data(), ne * 4);
   if (nt) std::memcpy(blob.data() + off_join, join.data(), nt * 4);
+  if (!jcnt.empty()) std::memcpy(blob.data() + off_jcnt, jcnt.data(), jcnt.size() * 4);
   if (no) std::memcpy(blob.data() + off_order, S.order.data(), no * 4);
   std::memcpy(blob.data() + off_order_off, S.offsets.data(), S.offsets.size() * 4);
   if (!lvl.empty()) std::memcpy(blob.data() + off_lvl, lvl.data(), lvl.size() * 4);
   std::memcpy(blob.data() + off_lvl_off, lvl_off.data(), lvl_off.size() * 4);
   if ((e = hipMalloc(&g->d_blob, blob_bytes)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(blob)"));
   if ((e = hipMalloc(&g->d_table, table.size() * 8)) != hipSuccess) return fail(hip_fail(e, "hipMalloc(table)"));
-  if ((e = hipMalloc(&g->d_arrivals, (nt ? nt : 1) * 4 * (size_t)mk::kArrivalStride)) != hipSuccess)
+  if ((e = hipMalloc(&g->d_arrivals, (g->n_counters ? g->n_counters : 1) * 4 * (size_t)mk::kArrivalStride)) !=
+      hipSuccess)
     return fail(hip_fail(e, "hipMalloc(arrivals)"));
   if ((e = hipMalloc(&g->d_ctrl, sizeof(mk::Ctrl))) != hipSuccess) return fail(hip_fail(e, "hipMalloc(ctrl)"));
   g->d_tasks = (mk_task_t*)(g->d_blob + off_tasks);
   g->d_edges = (uint32_t*)(g->d_blob + off_edges);
+  g->d_eslot = (uint32_t*)(g->d_blob + off_eslot);
   g->d_join = (uint32_t*)(g->d_blob + off_join);
+  g->d_jcnt = (uint32_t*)(g->d_blob + off_jcnt);
   g->d_order = (uint32_t*)(g->d_blob + off_order);
   g->d_order_off = (uint32_t*)(g->d_blob + off_order_off);
   g->d_rope = (float*)(g->d_blob + off_rope);

@@ -677,7 +677,7 @@ __device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_ta
 // One output element per thread.  The thread loads its o values and its head's
 // (m, l) for a block of chunks at once (one memory round trip per block of 16
 // chunks) and folds each block into a running (M, lam, O) with the same log-sum-exp
-// rule.  No LDS is used, so the workgroup's next GEMV tile can prefetch into it.
+// rule.  No LDS is used.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void task_combine(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   const int b = (int)d.reserved[0], h0 = (int)d.reserved[1], hc = (int)d.reserved[2];

@@ -19,9 +19,10 @@
 //  * the ring's first fill is issued before the dependency wait: weights are static,
 //    so the tile's first bytes arrive while its producers are still finishing;
 //  * one wave (the control wave) waits for the producers and stages the input rows
-//    in LDS (fp32, x * gamma) while the other waves' bulk prefetch is still landing:
-//    a wave's loads complete in issue order, so a poll or staging load queued behind
-//    the prefetch would only start once the prefetch had arrived;
+//    in LDS (fp32, x * gamma) while the other waves' rings are still landing: a
+//    wave's loads complete in issue order, so its poll queues only behind its own
+//    ring.  No larger prefetch is issued: requests queued in the workgroup's memory
+//    pipeline hold up the poll at the moment the producers finish;
 //  * a finished row is reduced across the wavefront with DPP (no LDS traffic) and
 //    parked in the register of lane (row % 64); parked results are stored 64 at a
 //    time, outside the streaming loop for every shape the workloads use.
@@ -38,7 +39,7 @@ namespace mk {
 constexpr uint32_t kWeightRange = 0xFFFFFFF0u;
 constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
 // The wave that waits for a tile's producers and stages its input (it streams its own
-// rows too, but issues no LDS prefetch: see gemv_issue_pf).
+// rows too).
 constexpr int kCtrlWave = kWaves - 1;
 // Cache-policy operand of a device-scope (sc1) load.
 constexpr int kCachePolicySC1 = 16;
@@ -64,19 +65,6 @@ __device__ __forceinline__ u32x4 gemv_load(const GemvGeom& g, int q, int kb, int
   // 32-bit byte offset into the matrix (every weight matrix is < 4 GiB).
   const uint32_t off = ((uint32_t)row * (uint32_t)g.KC + (uint32_t)chunk) * 16u;
   return __builtin_amdgcn_raw_buffer_load_b128(g.wr, past ? kPastEnd : off, 0, kCachePolicyNT);
-}
-
-// The same 16 bytes as gemv_load, copied straight into LDS at `dst` (+ 16 * lane):
-// a direct global-to-LDS load, so a prefetched row occupies no registers.
-__device__ __forceinline__ void gemv_load_lds(const GemvGeom& g, int q, int kb, int lane, char* dst) {
-  q = q < g.NQ ? q : g.NQ - 1;
-  const int j = g.silu ? (q >> 1) : q;
-  const int row = g.c0 + g.wave + kWaves * j + ((g.silu && (q & 1)) ? g.I : 0);
-  int chunk = kb * 64 + lane;
-  chunk = chunk < g.KC ? chunk : g.KC - 1;
-  const uint32_t off = ((uint32_t)row * (uint32_t)g.KC + (uint32_t)chunk) * 16u;
-  __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL char*)g.W + off),
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
 template <int BM, bool BF16>
@@ -112,47 +100,12 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
   }
 }
 
-// Two weight rows against one staged input row (batch 1): the input chunk is read
-// from LDS once for both rows (the LDS-resident rows are bound by LDS reads, and the
-// input is twice the bytes of a bf16 weight chunk).
-template <bool BF16>
-__device__ __forceinline__ void gemv_consume_pair(const u32x4 w0, const u32x4 w1, const float* xs, int chunk,
-                                                  bool valid, float& a0, float& a1) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  float f0[8], f1[8];
-  if (BF16) {
-    f0[0] = bf16_lo(w0.x); f0[1] = bf16_hi(w0.x); f0[2] = bf16_lo(w0.y); f0[3] = bf16_hi(w0.y);
-    f0[4] = bf16_lo(w0.z); f0[5] = bf16_hi(w0.z); f0[6] = bf16_lo(w0.w); f0[7] = bf16_hi(w0.w);
-    f1[0] = bf16_lo(w1.x); f1[1] = bf16_hi(w1.x); f1[2] = bf16_lo(w1.y); f1[3] = bf16_hi(w1.y);
-    f1[4] = bf16_lo(w1.z); f1[5] = bf16_hi(w1.z); f1[6] = bf16_lo(w1.w); f1[7] = bf16_hi(w1.w);
-  } else {
-    f0[0] = __uint_as_float(w0.x); f0[1] = __uint_as_float(w0.y); f0[2] = __uint_as_float(w0.z);
-    f0[3] = __uint_as_float(w0.w);
-    f1[0] = __uint_as_float(w1.x); f1[1] = __uint_as_float(w1.y); f1[2] = __uint_as_float(w1.z);
-    f1[3] = __uint_as_float(w1.w);
-    f0[4] = f0[5] = f0[6] = f0[7] = f1[4] = f1[5] = f1[6] = f1[7] = 0.f;
-  }
-  const float m = valid ? 1.f : 0.f;  // a masked chunk contributes 0
-  const f32x4* xb = (const f32x4*)(xs + (valid ? chunk : 0) * VEC);
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int e = 0; e < VEC / 4; ++e) {
-    const f32x4 xv = xb[e];
-    s0 = fmaf(f0[4 * e + 0], xv.x, s0); s1 = fmaf(f1[4 * e + 0], xv.x, s1);
-    s0 = fmaf(f0[4 * e + 1], xv.y, s0); s1 = fmaf(f1[4 * e + 1], xv.y, s1);
-    s0 = fmaf(f0[4 * e + 2], xv.z, s0); s1 = fmaf(f1[4 * e + 2], xv.z, s1);
-    s0 = fmaf(f0[4 * e + 3], xv.w, s0); s1 = fmaf(f1[4 * e + 3], xv.w, s1);
-  }
-  a0 = fmaf(s0, m, a0);
-  a1 = fmaf(s1, m, a1);
-}
-
 // Wait for the tile's producers and stage its input rows 0 .. nb-1 (x * gamma with
 // RMS_NORM_INPUT) into LDS, both on the control wave alone (spread: the copies are
-// shared by every wave, see below), then meet the other waves at one barrier; returns r_b (1 without the norm) in rs[], or false if the step was
-// abandoned.  The control wave has issued no LDS prefetch, so its poll and its staging
-// loads queue only behind its own weight ring, not behind the tile's bulk prefetch,
-// which keeps arriving meanwhile.  The input rows are copied into LDS by device-scope
+// shared by every wave, see below), then meet the other waves at one barrier; returns
+// r_b (1 without the norm) in rs[], or false if the step was abandoned.  The control
+// wave's poll and staging loads queue only behind its own weight ring.  The input
+// rows are copied into LDS by device-scope
 // (sc1) global-to-LDS loads, up to 63 KB per round trip; gamma is loaded alongside
 // into registers in blocks of GB chunks of 4 values per lane; the norm's sum of
 // squares is then taken from LDS and reduced within the wave.
@@ -168,8 +121,7 @@ __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t,
     sm.flag = ok;
     sm.t_ready = clock100();
   }
-  // spread (no norm, no LDS rows in this tile): no wave has a bulk prefetch queued
-  // ahead of its loads, so once the control wave has seen the producers every wave
+  // spread (no norm): once the control wave has seen the producers every wave
   // copies its share of the input (one wave's copies alone take a round trip per
   // ~20 KB).  Both cases share one copy loop: a second copy site made the compiler's
   // wait counts in the streaming loops drain the ring at every row.
@@ -226,9 +178,9 @@ __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t,
     if (a.trace != nullptr && ctrl && lane == 0) sm.t_mark[2] = clock100();
   }
   __syncthreads();
-  // Every wave now waits for its own ring and LDS prefetch.  Written as the builtin
+  // Every wave now waits for its own ring and input copies.  Written as the builtin
   // (not inline asm) so that the compiler's wait-count tracking sees it: otherwise
-  // the prefetch's pending LDS writes would make it put a full wait before every LDS
+  // the copies' pending LDS writes would make it put a full wait before every LDS
   // read of the staged input inside the streaming loop, draining the ring each step.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if (sm.flag == 0) return false;
@@ -283,49 +235,6 @@ __device__ __forceinline__ GemvGeom gemv_geom(const LaunchArgs& a, const mk_task
   return g;
 }
 
-// Static-input prefetch into LDS of a tile whose rows have KBR kblocks (compile-time
-// streaming path): when the whole batch is staged in one pass and the wave has at most
-// 64 rows, the LDS after the staged input (xfl floats) holds the wave's first PF
-// whole rows at pfw.  One definition serves the tile itself and a prefetch issued
-// while the workgroup still runs its previous task.
-struct GemvPf {
-  int PF;
-  int xfl;
-  char* pfw;
-  int cap;  // whole rows that fit one wave's share (the same for every wave; 0: none)
-};
-
-template <int KBR>
-__device__ __forceinline__ GemvPf gemv_pf_plan(const GemvGeom& g, int B, int bp, Smem& sm) {
-  GemvPf p{0, 0, nullptr};
-  if (B <= bp && g.NQ <= 64) {
-    p.xfl = (B * g.K + 3) & ~3;
-    const int per_wave = ((kSmemBytes - 4 * p.xfl) / kWaves) & ~1023;
-    const int pf = per_wave / (KBR * 1024);
-    p.cap = pf;
-    p.PF = pf < g.NQ ? pf : g.NQ;
-    p.pfw = (char*)(sm.xs + p.xfl) + g.wave * per_wave;
-  }
-  return p;
-}
-
-// Issue the LDS prefetch of the tile's PF-row blocks.  The control wave (which waits
-// for the producers and stages the input) issues none, so that nothing queues ahead of
-// its poll and its staging loads: the other waves issue their own rows and, round
-// robin, the control wave's (gc, pc: its geometry and plan).  Every wave waits for
-// its loads and meets a barrier before any LDS-resident row is read.
-template <int KBR>
-__device__ __forceinline__ void gemv_issue_pf(const GemvGeom& g, const GemvPf& p, const GemvGeom& gc,
-                                              const GemvPf& pc, int lane) {
-  if (g.wave == kCtrlWave) return;
-  for (int q = 0; q < p.PF; ++q)
-#pragma unroll
-    for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(g, q, kb, lane, p.pfw + (q * KBR + kb) * 1024);
-  for (int q = g.wave; q < pc.PF; q += kCtrlWave)
-#pragma unroll
-    for (int kb = 0; kb < KBR; ++kb) gemv_load_lds(gc, q, kb, lane, pc.pfw + (q * KBR + kb) * 1024);
-}
-
 // Batch rows staged per pass of a tile with inner dimension K.
 template <int BM>
 __device__ __forceinline__ int gemv_batch_pass(int K) {
@@ -333,27 +242,11 @@ __device__ __forceinline__ int gemv_batch_pass(int K) {
   return bp < BM ? bp : BM;
 }
 
-// Issue the LDS prefetch of GEMV tile d (rows of KBR kblocks) ahead of time, while the
-// workgroup still runs a task that uses at most lds_used bytes at the start of the
-// LDS.  Returns whether it was issued; the tile then skips its own prefetch.
-template <int BM, bool BF16, int KBR>
-__device__ __forceinline__ bool gemv_prefetch_ahead(const LaunchArgs& a, const mk_task_t& d, int lds_used,
-                                                    Smem& sm) {
-  const int bp = gemv_batch_pass<BM>(d.k);
-  const GemvGeom g = gemv_geom<BF16>(a, d, wave_id());
-  const GemvPf p = gemv_pf_plan<KBR>(g, d.m, bp, sm);
-  if (4 * p.xfl < lds_used) return false;
-  const GemvGeom gc = gemv_geom<BF16>(a, d, kCtrlWave);
-  const GemvPf pc = gemv_pf_plan<KBR>(gc, d.m, bp, sm);
-  gemv_issue_pf<KBR>(g, p, gc, pc, lane_id());
-  return true;
-}
-
 // A row is SEG segments of KBT kblocks (compile time; KBT = 0: any K, one kblock at a
 // time); RPG rows are in flight per wave.  Ring slot (r, kb) cycles through kblock
 // s * KBT + kb of row r for s = 0 .. SEG-1, then moves to the row RPG ahead.
 template <int BM, bool BF16, int KBT, int SEG, int RPG>
-__device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm, bool pre) {
+__device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   constexpr int KBS = KBT > 0 ? KBT : 1;
   const int lane = lane_id();
   const GemvGeom g = gemv_geom<BF16>(a, d, wave_id());
@@ -368,35 +261,23 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
 
   for (int b0 = 0; b0 < B; b0 += bp) {
     const int nb = (B - b0) < bp ? (B - b0) : bp;
-    // Static-input prefetch into LDS (gemv_pf_plan), loaded before the dependency
-    // wait, or already in flight when the previous task issued it (pre).  Those rows
-    // are consumed last, after the register ring has streamed the rest.  The register
-    // ring's first rows are issued before the LDS rows: loads complete in issue order,
-    // so the ring never waits behind the prefetch.
-    constexpr int KBR = KBS * SEG;  // kblocks per row (compile-time path)
-    GemvPf pf{0, 0, nullptr}, pfc{0, 0, nullptr};
-    GemvGeom gc = g;
-    if (KBT > 0 && b0 == 0) {
-      pf = gemv_pf_plan<KBR>(g, B, bp, sm);
-      gc = gemv_geom<BF16>(a, d, kCtrlWave);
-      pfc = gemv_pf_plan<KBR>(gc, B, bp, sm);
-    }
-    const int PF = pf.PF;
-    char* const pfw = pf.pfw;
+    // The register ring's first rows are loaded before the dependency wait (weights are
+    // static).  Nothing larger is issued ahead: a bulk prefetch queued in the same
+    // memory pipeline delays the control wave's poll by microseconds at the moment the
+    // producers finish, which costs more than the prefetch saves.
     u32x4 buf[RPG][KBS];
-    if (KBT > 0 && g.NQ > PF) {
+    if (KBT > 0 && g.NQ > 0) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r)
 #pragma unroll
-        for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, PF + r, kb, lane);
+        for (int kb = 0; kb < KBS; ++kb) buf[r][kb] = gemv_load(g, r, kb, lane);
     }
-    if (KBT > 0 && b0 == 0 && !pre) gemv_issue_pf<KBR>(g, pf, gc, pfc, lane);
     float rs[BM];
     // One call site for every batch pass (later passes have no producers to wait
     // for): staging code duplicated on two paths into the streaming loop made the
     // compiler's wait counts there drain the whole ring at every row.
     if (!gemv_wait_stage<BM, BF16>(a, t, b0 == 0 ? d.remaining_deps : 0, x + (size_t)b0 * g.K, aux, norm, g.K, nb,
-                                   a.rms_eps, sm, rs, !norm && pf.cap == 0))
+                                   a.rms_eps, sm, rs, !norm))
       return;
     if (b0 == 0) trace_mark(a, sm, 0);
     float park[BM];
@@ -404,9 +285,9 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     for (int b = 0; b < BM; ++b) park[b] = 0.f;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // nothing pending into LDS (ring already landed)
     if (g.NQ > 0) {
-      const int iters_ring = (g.NQ - PF + RPG - 1) / RPG;
+      const int iters_ring = (g.NQ + RPG - 1) / RPG;
       for (int it = 0; it < iters_ring; ++it) {
-        const int q0 = PF + it * RPG;
+        const int q0 = it * RPG;
         // Short rows: the compiler may keep the staged input in registers across rows.
         // Long rows: an opaque offset keeps the LDS reads inside the loop instead of
         // pinning 8 registers per kblock.
@@ -449,52 +330,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
         }
       }
     }
-    // The LDS-resident rows (PF > 0 only when the whole batch is staged in one pass
-    // and the wave has at most 64 rows, so the final flush covers them).  They were
-    // loaded by other waves (the control wave's) or by the previous task: every wave
-    // waits for its own loads, then all meet, before any of them is read.
-    if (KBT > 0 && b0 == 0 && B <= bp) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-    }
     if (g.NQ > 0) {
-      if (KBT > 0) {
-        int q = 0;
-        if constexpr (BM == 1 && KBR <= 8) {
-          for (; q + 1 < PF; q += 2) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll 2
-            for (int kb = 0; kb < KBR; ++kb) {
-              const u32x4 w0 = *(const u32x4*)(pfw + (q * KBR + kb) * 1024 + 16 * lane);
-              const u32x4 w1 = *(const u32x4*)(pfw + ((q + 1) * KBR + kb) * 1024 + 16 * lane);
-              const int chunk = kb * 64 + lane;
-              gemv_consume_pair<BF16>(w0, w1, sm.xs, chunk, chunk < g.KC, a0, a1);
-            }
-            const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(a0)), 63));
-            const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(a1)), 63));
-            park[0] = (lane == (q & 63)) ? v0 * rs[0] : park[0];
-            park[0] = (lane == ((q + 1) & 63)) ? v1 * rs[0] : park[0];
-          }
-        }
-        for (; q < PF; ++q) {
-          float acc[BM];
-#pragma unroll
-          for (int b = 0; b < BM; ++b) acc[b] = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < KBR; ++kb) {
-            const u32x4 wv = *(const u32x4*)(pfw + (q * KBR + kb) * 1024 + 16 * lane);
-            const int chunk = kb * 64 + lane;
-            gemv_consume<BM, BF16>(wv, sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
-          }
-#pragma unroll
-          for (int b = 0; b < BM; ++b) {
-            if (b < nb) {
-              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(acc[b])), 63));
-              park[b] = (lane == (q & 63)) ? v * rs[b] : park[b];
-            }
-          }
-        }
-      }
       if (b0 == 0) trace_mark(a, sm, 1);
       gemv_flush<BM>(g, park, ((g.NQ - 1) >> 6) << 6, nb, resid, (const float*)aux, y, N, b0);
     }
