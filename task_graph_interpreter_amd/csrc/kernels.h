@@ -68,7 +68,7 @@ __device__ __forceinline__ void run_task_spec(const LaunchArgs& a, const mk_task
   switch (d.op_id) {
     case MK_OP_GEMV: gemv_spec<S>(a, d, t, sm); break;
     case MK_OP_ATTENTION_APPEND: task_append(a, d, t, sm); break;
-    case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16, S::BM == 32, (S::BM > 1)>(a, d, t, sm); break;
+    case MK_OP_ATTENTION_PARTIAL: task_partial_kv<S::KVBF16, S::BM == 32, (S::BM > 1 ? 2 : 1)>(a, d, t, sm); break;
     case MK_OP_ATTENTION_COMBINE: task_combine(a, d, t, sm); break;
     case MK_OP_MEMCPY: task_memcpy(a, d, t, sm); break;
     case MK_OP_RMSNORM: task_rmsnorm(a, d, t, sm); break;

@@ -645,17 +645,15 @@ __device__ __forceinline__ void partial_heads(const LaunchArgs& a, const mk_task
 
 // Lanes per cache row (head_dim * element size / 16) as a compile-time constant for
 // the common shapes (head_dim 64 and 128), else a run-time value.
-// Blocks of 16 keys in flight per wave in the matrix-core pass.
-constexpr int kAttnRing = 2;
-
-// MFMA: the matrix-core pass (kernels for batches above 1, whose chunks are long
-// enough for the fold's VALU work to bound the pass; the batch-1 kernels keep the
-// 16-lane fold, which is as fast on their short chunks).
-template <bool KVBF16, bool BATCHED, bool MFMA>
+// NS > 0: the matrix-core pass with a ring of NS blocks of 16 keys per wave (the
+// kernels pass 2 for batches above 1; 1 for batch 1, whose chunks give each wave
+// about one block), for a bf16 cache with head_dim 64 or 128; otherwise, and for
+// other shapes, the 16-lane fold.
+template <bool KVBF16, bool BATCHED, int NS>
 __device__ __forceinline__ void task_partial_kv(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
-  if constexpr (KVBF16 && MFMA) {
-    if (d.n == 128) return partial_heads_mfma<128, kAttnRing>(a, d, t, sm);
-    if (d.n == 64) return partial_heads_mfma<64, kAttnRing>(a, d, t, sm);
+  if constexpr (KVBF16 && NS > 0) {
+    if (d.n == 128) return partial_heads_mfma<128, NS>(a, d, t, sm);
+    if (d.n == 64) return partial_heads_mfma<64, NS>(a, d, t, sm);
   }
   // R rounds per batch: 2 for chunks of at most two rounds, else 4.
   const int lpk = d.n * (KVBF16 ? 2 : 4) / 16;

@@ -100,65 +100,55 @@ __device__ __forceinline__ void gemv_consume(const u32x4 w, const float* xs, int
   }
 }
 
-// Wait for the tile's producers and stage its input rows 0 .. nb-1 (x * gamma with
-// RMS_NORM_INPUT) into LDS, both on the control wave alone (spread: the copies are
-// shared by every wave, see below), then meet the other waves at one barrier; returns
-// r_b (1 without the norm) in rs[], or false if the step was abandoned.  The control
-// wave's poll and staging loads queue only behind its own weight ring.  The input
-// rows are copied into LDS by device-scope
-// (sc1) global-to-LDS loads, up to 63 KB per round trip; gamma is loaded alongside
-// into registers in blocks of GB chunks of 4 values per lane; the norm's sum of
-// squares is then taken from LDS and reduced within the wave.
+// Wait for the tile's producers (the control wave polls), then stage its input rows
+// 0 .. nb-1 into LDS on every wave: each thread copies its share of the rows with
+// device-scope (sc1) global-to-LDS loads and, with RMS_NORM_INPUT, scales the same
+// elements by gamma (loaded meanwhile) and sums their squares, so no wave waits for
+// another's copies; the waves' partial sums meet in LDS at the closing barrier.
+// Returns r_b (1 without the norm) in rs[], or false if the step was abandoned.  The
+// control wave's poll queues only behind its own weight ring.
 template <int BM, bool GBF16>
 __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t, int32_t indeg, const float* x,
                                                 const char* gamma, bool norm, int K, int nb, float eps, Smem& sm,
-                                                float rs[BM], bool spread) {
+                                                float rs[BM]) {
   const bool ctrl = wave_id() == kCtrlWave;
-  const int lane = lane_id();
-  uint32_t ok = 1;
+  const int lane = lane_id(), w = wave_id();
   if (ctrl && lane == 0) {
-    ok = poll_deps(a, t, indeg);
-    sm.flag = ok;
+    sm.flag = poll_deps(a, t, indeg);
     sm.t_ready = clock100();
   }
-  // spread (no norm): once the control wave has seen the producers every wave
-  // copies its share of the input (one wave's copies alone take a round trip per
-  // ~20 KB).  Both cases share one copy loop: a second copy site made the compiler's
-  // wait counts in the streaming loops drain the ring at every row.
-  if (spread) {
-    __syncthreads();
-    ok = sm.flag;
-  }
-  ok = __builtin_amdgcn_readfirstlane(ok);
-  if ((ctrl || spread) && ok) {
+  __syncthreads();
+  const uint32_t ok = __builtin_amdgcn_readfirstlane(sm.flag);
+  float* part = sm.red + kRedFloats - 128;  // [BM][kWaves] partial sums of squares
+  if (ok) {
     const int K4 = K >> 2;
-    const int cf = spread ? wave_id() * 64 : 0, cs = spread ? kThreads : 64;
     for (int b = 0; b < nb; ++b)
-      for (int c = cf; c < K4; c += cs)
+      for (int c = w * 64; c < K4; c += kThreads)
         if (c + lane < K4)
           __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL f32x4*)x + (size_t)b * K4 + c + lane),
                                            (__attribute__((address_space(3))) void*)(sm.xs + (size_t)b * K + 4 * c),
                                            16, 0, kCachePolicySC1);
-    // gamma (weight dtype) in raw form: 8 bytes per 4 values in bf16, 16 in fp32.
+    // gamma (weight dtype) in raw form: 8 bytes per 4 values in bf16, 16 in fp32; the
+    // thread's chunks are k4 = 64 w + lane + 512 j, the ones it copied.
     typedef typename std::conditional<GBF16, u32x2, u32x4>::type graw_t;
-    constexpr int GB = 16;
+    constexpr int GB = 8;
     for (int b = 0; b < nb; ++b) {
       f32x4* xo = (f32x4*)(sm.xs + (size_t)b * K);
       float ss = 0.f;
-      for (int c0 = 0; c0 < K4; c0 += 64 * GB) {
+      for (int c0 = w * 64 + lane; c0 < K4; c0 += kThreads * GB) {
         graw_t gv[GB];
         if (norm) {
 #pragma unroll
           for (int u = 0; u < GB; ++u) {
-            const int k4 = c0 + u * 64 + lane;
+            const int k4 = c0 + u * kThreads;
             gv[u] = ldg<graw_t>(gamma, k4 < K4 ? k4 : 0);
           }
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row's LDS copy has landed
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this thread's LDS copies have landed
         if (norm) {
 #pragma unroll
           for (int u = 0; u < GB; ++u) {
-            const int k4 = c0 + u * 64 + lane;
+            const int k4 = c0 + u * kThreads;
             if (k4 < K4) {
               f32x4 v = xo[k4];
               ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
@@ -171,21 +161,30 @@ __device__ __forceinline__ bool gemv_wait_stage(const LaunchArgs& a, uint32_t t,
           }
         }
       }
-      if (norm) ss = wave_sum(ss);
-      if (ctrl && lane == 0) sm.red[b] = norm ? 1.0f / sqrtf(ss / (float)K + eps) : 1.f;
+      if (norm) {
+        ss = wave_sum(ss);
+        if (lane == 0) part[b * kWaves + w] = ss;
+      }
     }
-    // Trace mode: when the input was staged (mark 2; marks 0 and 1 are thread 0's).
-    if (a.trace != nullptr && ctrl && lane == 0) sm.t_mark[2] = clock100();
   }
   __syncthreads();
+  // Trace mode: when the input was staged (mark 2; marks 0 and 1 are thread 0's).
+  if (a.trace != nullptr && ctrl && lane == 0) sm.t_mark[2] = clock100();
   // Every wave now waits for its own ring and input copies.  Written as the builtin
   // (not inline asm) so that the compiler's wait-count tracking sees it: otherwise
   // the copies' pending LDS writes would make it put a full wait before every LDS
   // read of the staged input inside the streaming loop, draining the ring each step.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if (sm.flag == 0) return false;
+  if (ok == 0) return false;
 #pragma unroll
-  for (int b = 0; b < BM; ++b) rs[b] = b < nb ? sm.red[b] : 1.f;
+  for (int b = 0; b < BM; ++b) {
+    float tot = 0.f;
+    if (norm && b < nb) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) tot += part[b * kWaves + ww];
+    }
+    rs[b] = (norm && b < nb) ? 1.0f / sqrtf(tot / (float)K + eps) : 1.f;
+  }
   return true;
 }
 
@@ -277,7 +276,7 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
     // for): staging code duplicated on two paths into the streaming loop made the
     // compiler's wait counts there drain the whole ring at every row.
     if (!gemv_wait_stage<BM, BF16>(a, t, b0 == 0 ? d.remaining_deps : 0, x + (size_t)b0 * g.K, aux, norm, g.K, nb,
-                                   a.rms_eps, sm, rs, !norm))
+                                   a.rms_eps, sm, rs))
       return;
     if (b0 == 0) trace_mark(a, sm, 0);
     float park[BM];
