@@ -310,6 +310,7 @@ def main():
     ap.add_argument("--kv-chunk", type=int, default=0, help="override the workload's split-KV chunk (keys)")
     ap.add_argument("--gemv-tiles", type=int, default=0, help="override the workload's GEMV tiles per matmul")
     ap.add_argument("--gemv-config", type=int, default=-1, help="override the GEMV variant (1 vector, 2 MFMA)")
+    ap.add_argument("--packed", type=int, default=-1, help="override the weight layout (0 row-major, 1 tile16)")
     ap.add_argument("--greedy-tokens", type=int, default=-1,
                     help="greedy decode of N tokens after the timed step (time between tokens); "
                          "default 256 at batch 1, else 0")
@@ -350,6 +351,8 @@ def main():
         w = w.replace(gemv_tiles=args.gemv_tiles)
     if args.gemv_config >= 0:
         w = w.replace(gemv_config=args.gemv_config)
+    if args.packed >= 0:
+        w = w.replace(packed=args.packed)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: filling {w.weight_bytes_per_step() / 1e9:.2f} GB weights + caches")
     inp = DeviceInputs(w)
@@ -487,7 +490,8 @@ def main():
     n_greedy = args.greedy_tokens if args.greedy_tokens >= 0 else (256 if w.batch == 1 else 0)
     greedy = greedy_run(w, inp, n_greedy, stream) if n_greedy > 0 else None
 
-    traffic = measured_traffic(w.name) if not (args.kv_chunk or args.gemv_tiles or args.gemv_config >= 0) else None
+    traffic = (measured_traffic(w.name)
+               if not (args.kv_chunk or args.gemv_tiles or args.gemv_config >= 0 or args.packed >= 0) else None)
     name_timed = g.mk_graph_kernel_name()
     g.close()
     del scratch

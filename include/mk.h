@@ -150,11 +150,11 @@ typedef struct mk_model_cfg {
 #define MK_LOWER_SAMPLE 2
 /*   MK_LOWER_PACKED_WEIGHTS: the five matrices of every layer and the lm_head (W_qkv,
  *     W_o, W_gate_up, W_down, W_lm; not the embedding) are passed in the 16-row tile
- *     layout that mk_pack_matrix writes.  Needs gemv_config MK_GEMV_BF16_MFMA and batch
- *     <= 8 (the matrix-core tile for small batches reads that layout one contiguous
- *     kilobyte per wave and k-step); MK_ERR_INVALID otherwise.  The descriptors are the
- *     same as without the bit: the layout is a property of the weight buffers, and the
- *     results are bitwise those of the row-major weights. */
+ *     layout that mk_pack_matrix writes.  Needs gemv_config MK_GEMV_BF16_MFMA (the
+ *     matrix-core tiles read that layout one contiguous kilobyte per wave and k-step);
+ *     MK_ERR_INVALID otherwise.  The descriptors are the same as without the bit: the
+ *     layout is a property of the weight buffers, and the results are bitwise those of
+ *     the row-major weights. */
 #define MK_LOWER_PACKED_WEIGHTS 4
 
 /* Weights in canonical order (buffer-table section of the page: append-only, one

@@ -59,7 +59,7 @@ class Workload:
     join_nodes: int = 1
     unfused: int = 0  # 1: lower without the epilogue-fusion pass (standalone RMSNORM tasks)
     sample: int = 0   # 1: SAMPLE tasks after the lm_head (a whole greedy step per launch)
-    packed: int = 0   # 1: matrices in the library's 16-row tile layout (MFMA GEMV, batch <= 8)
+    packed: int = 0   # 1: matrices in the library's 16-row tile layout (MFMA GEMV only)
     seed: int = 0
     meta: dict = field(default_factory=dict, compare=False)
 

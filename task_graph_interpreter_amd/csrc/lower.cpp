@@ -327,8 +327,8 @@ int validate_cfg(const mk_model_cfg* c) {
   }
   if (c->options & ~(MK_LOWER_UNFUSED | MK_LOWER_SAMPLE | MK_LOWER_PACKED_WEIGHTS))
     return set_error(MK_ERR_INVALID, "unknown bit in options");
-  if ((c->options & MK_LOWER_PACKED_WEIGHTS) && !(c->gemv_config == MK_GEMV_BF16_MFMA && c->batch <= 8))
-    return set_error(MK_ERR_INVALID, "MK_LOWER_PACKED_WEIGHTS needs the MFMA GEMV (gemv_config 2) and batch <= 8");
+  if ((c->options & MK_LOWER_PACKED_WEIGHTS) && c->gemv_config != MK_GEMV_BF16_MFMA)
+    return set_error(MK_ERR_INVALID, "MK_LOWER_PACKED_WEIGHTS needs the MFMA GEMV (gemv_config 2)");
   if (7ll + 15ll * c->n_layers + ((c->options & MK_LOWER_UNFUSED) ? 4ll * c->n_layers + 1 : 0) > 0xFFFF)
     return set_error(MK_ERR_INVALID, "more than 65535 buffers");
   // Limits of the device task bodies: GEMV rows are streamed in 16-byte pieces and an

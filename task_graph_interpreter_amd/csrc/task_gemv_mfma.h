@@ -56,6 +56,7 @@ struct MfmaGeom {
   int c0, cols, I;   // first output column, tile width, up-row offset (SILU_MUL)
   int silu;
   int nc;            // chunks
+  int packed;        // weights in the 16-row tile layout of mk_pack_matrix
 };
 
 // First weight row of global block gb (SILU_MUL: even blocks gate, odd blocks up).
@@ -64,11 +65,20 @@ __device__ __forceinline__ int mfma_block_row(const MfmaGeom& g, int gb) {
   return g.c0 + 16 * (gb >> 1) + ((gb & 1) ? g.I : 0);
 }
 
-// One lane's 16 bytes of A for block gb, chunk c, k-step s (0..7).
+// One lane's 16 bytes of A for block gb, chunk c, k-step s (0..7): row-major, lane l
+// reads row l % 16 at k = 256 c + 32 s + 8 (l / 16); in the tile layout the k-step's
+// 1 KB tile of the block sits at 1024 (8 c + s), lane l's bytes at 16 l (the same
+// values).  Byte offsets < 4 GiB (checked when lowering).
 __device__ __forceinline__ u32x4 mfma_wload(const MfmaGeom& g, int gb, int c, int s, int lane) {
-  const uint32_t row = (uint32_t)(mfma_block_row(g, gb) + (lane & 15));
-  const uint32_t k = (uint32_t)c * kMfmaKC + (uint32_t)s * 32u + 8u * (uint32_t)(lane >> 4);
-  const uint32_t off = (row * g.K + k) * 2u;  // < 4 GiB (checked when lowering)
+  const uint32_t row0 = (uint32_t)mfma_block_row(g, gb);
+  uint32_t off;
+  if (g.packed) {
+    off = row0 * g.K * 2u + ((uint32_t)c * (kMfmaKC / 32) + (uint32_t)s) * 1024u + 16u * (uint32_t)lane;
+  } else {
+    const uint32_t row = row0 + (uint32_t)(lane & 15);
+    const uint32_t k = (uint32_t)c * kMfmaKC + (uint32_t)s * 32u + 8u * (uint32_t)(lane >> 4);
+    off = (row * g.K + k) * 2u;
+  }
   return __builtin_nontemporal_load((const MK_GLOBAL u32x4*)((const MK_GLOBAL char*)g.W + off));
 }
 
@@ -298,6 +308,7 @@ __device__ __forceinline__ void gemv_mfma(const LaunchArgs& a, const mk_task_t& 
   g.I = (int)d.reserved[2];
   g.silu = (d.flags & MK_FLAG_SILU_MUL) ? 1 : 0;
   g.nc = d.k / kMfmaKC;
+  g.packed = a.wpacked ? 1 : 0;
   const float* x = (const float*)resolve(a, d.in_buf[0]);
   const char* aux = d.in_buf[2] != 0xFFFF ? resolve(a, d.in_buf[2]) : nullptr;
   float* y = (float*)resolve(a, d.out_buf);

@@ -246,6 +246,7 @@ __device__ __forceinline__ void gemv_mfma_small(const LaunchArgs& a, const mk_ta
   g.I = (int)d.reserved[2];
   g.silu = (d.flags & MK_FLAG_SILU_MUL) ? 1 : 0;
   g.nc = 0;
+  g.packed = a.wpacked ? 1 : 0;
   const char* x = resolve(a, d.in_buf[0]);
   const char* aux = d.in_buf[2] != 0xFFFF ? resolve(a, d.in_buf[2]) : nullptr;
   float* y = (float*)resolve(a, d.out_buf);

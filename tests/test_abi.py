@@ -140,10 +140,8 @@ def test_packed_weight_option_lowers_the_same_graph(name):
     assert np.array_equal(a.edges(), b.edges())
 
 
-@pytest.mark.parametrize("over", [dict(), dict(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1),
-                                  dict(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, batch=9,
-                                       kv_len=(128,) * 9)])
-def test_packed_weight_option_needs_the_small_batch_mfma_tile(over):
+@pytest.mark.parametrize("over", [dict(), dict(weight_dtype="bf16", kv_dtype="bf16", gemv_config=1)])
+def test_packed_weight_option_needs_the_mfma_gemv(over):
     cfg, keep = _cfg(workloads.tiny().replace(packed=1), **over)
     with pytest.raises(mk.MkError) as e:
         mk.mk_plan(cfg)

@@ -199,11 +199,11 @@ def test_pack_matrix_layout(rows, cols):
     assert np.array_equal(got, want.reshape(-1))
 
 
-@pytest.mark.parametrize("case", ["b8", "b8_wide", "b1", "b3_ragged"])
+@pytest.mark.parametrize("case", ["b8", "b8_wide", "b1", "b3_ragged", "b32", "b40", "b32_wide"])
 def test_tiny_mfma_packed_weights_bitwise_row_major(case):
-    # The small-batch matrix-core tile reading the tile layout (MK_LOWER_PACKED_WEIGHTS)
-    # does the same products in the same order as with row-major weights: every
-    # activation and the logits are bitwise equal; the packed run also against the oracle.
+    # The matrix-core tiles reading the tile layout (MK_LOWER_PACKED_WEIGHTS) do the
+    # same products in the same order as with row-major weights: every activation and
+    # the logits are bitwise equal; the packed run also against the oracle.
     w = workloads.tiny().replace(weight_dtype="bf16", kv_dtype="bf16", gemv_config=2, kv_capacity=128,
                                  name=f"tiny_mfma_{case}", **MFMA_CASES[case])
     _say(f"tiny MFMA GEMV {case}, packed weights vs row-major")
@@ -211,7 +211,7 @@ def test_tiny_mfma_packed_weights_bitwise_row_major(case):
     logits = run.step("persistent")
     acts = run.activations()
     runp = MkRun(w.replace(packed=1, name=f"tiny_mfma_{case}_packed"), inputs=run.inp)
-    assert runp.graph.mk_graph_kernel_name().startswith("mfma8_")
+    assert runp.graph.mk_graph_kernel_name().startswith("mfma8_" if w.batch <= 8 else "mfma_")
     logits_p = runp.step("persistent")
     acts_p = runp.activations()
     assert np.array_equal(logits_p, logits), "packed and row-major logits differ"
