@@ -182,10 +182,18 @@ typedef struct mk_plan_info {
   uint64_t kv_layer_bytes;   /* bytes of one layer's K (or V) cache slab */
 } mk_plan_info;
 
+/* Validate `cfg` and size the lowered graph: task, edge, buffer and level counts, and
+ * the activation scratch the caller allocates ("Mega kernel initial": the lowering
+ * section fans each op out into tiles, and the buffer-table section allocates each
+ * op's output on demand; here every output gets its own span of one scratch block).
+ * Host only; touches no GPU.  Errors: MK_ERR_ABI, MK_ERR_INVALID. */
 int mk_plan(const mk_model_cfg* cfg, mk_plan_info* out);
 
-/* Host-only lowering (no GPU calls): the descriptor array and CSR edge array that
- * mk_build_graph would upload.  Arrays stay owned by the mk_lowered object. */
+/* Host-only lowering (no GPU calls; "Mega kernel initial": the lowering section --
+ * fan-out into column tiles, parents tracked per column range, flattened to an edge
+ * array -- and the descriptor section): the descriptor array and CSR edge array that
+ * mk_build_graph would upload.  Arrays stay owned by the mk_lowered object.  Errors:
+ * MK_ERR_ABI, MK_ERR_INVALID, MK_ERR_NOMEM. */
 int mk_lower(const mk_model_cfg* cfg, mk_lowered** out);
 int mk_lowered_tasks(const mk_lowered* g, const mk_task_t** tasks, uint32_t* n);
 int mk_lowered_edges(const mk_lowered* g, const uint32_t** edges, uint32_t* n);
@@ -234,13 +242,17 @@ int mk_pack_matrix(const void* src_dev, void* dst_dev, int32_t rows, int32_t col
 int mk_graph_tasks(const mk_graph* g, const mk_task_t** tasks, uint32_t* n);
 int mk_graph_edges(const mk_graph* g, const uint32_t** edges, uint32_t* n);
 
-/* One decode step as ONE persistent-kernel launch, enqueued on `stream` (no host
- * synchronisation).  Device pointers: tokens_dev int32[batch]; positions_dev
+/* One decode step as ONE persistent-kernel launch ("Megakernels", runhoid.com: "Hoid's
+ * approach to megakernels" -- one kernel that interprets the task list, each block
+ * waiting only on its own producers -- and iceberg layer 6), enqueued on `stream` (no
+ * host synchronisation).  Device pointers: tokens_dev int32[batch]; positions_dev
  * int32[batch]; kcache_dev / vcache_dev [n_layers][batch][n_kv_heads][kv_capacity]
  * [head_dim] in kv_dtype (slot positions[b] of every layer is overwritten with the new
  * token's rotated k and its v); logits_dev float32[batch][vocab].  The step reads the
  * cache slots [0, positions[b]].  Out-of-range positions set the device status
- * (mk_status) and leave the outputs of the affected sequence undefined. */
+ * (mk_status) and leave the outputs of the affected sequence undefined.  Errors:
+ * MK_ERR_INVALID (NULL graph or pointer, graph built without scratch), MK_ERR_ALIGN
+ * (buffers not 16-byte aligned; tokens and positions 4), MK_ERR_HIP (launch). */
 int mk_decode_step(mk_graph* g, void* stream, const int32_t* tokens_dev, const int32_t* positions_dev,
                    void* kcache_dev, void* vcache_dev, float* logits_dev);
 
@@ -264,7 +276,9 @@ int mk_decode_step_noalloc(mk_graph* g, void* stream, const int32_t* tokens_dev,
                            void* kcache_dev, void* vcache_dev, float* logits_dev);
 
 /* The same step with the same task bodies and descriptors, one kernel launch per op
- * (stream order instead of readiness counters): the per-op-launch baseline. */
+ * (stream order instead of readiness counters): the per-op-launch baseline the pages
+ * measure against ("Megakernels", runhoid.com, Introduction: the launch gaps and tails
+ * of one kernel per op).  Same errors as mk_decode_step. */
 int mk_decode_step_per_op(mk_graph* g, void* stream, const int32_t* tokens_dev,
                           const int32_t* positions_dev, void* kcache_dev, void* vcache_dev,
                           float* logits_dev);
