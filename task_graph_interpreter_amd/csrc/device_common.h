@@ -35,6 +35,8 @@ constexpr uint32_t kJoinShards = 8;
 // operand of a buffer load that streams (non-temporal).
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kCachePolicyNT = 2;
+// Cache-policy operand of a device-scope (sc1) load.
+constexpr int kCachePolicySC1 = 16;
 
 // Buffer-table entry tags (top byte): 0 = absolute device pointer; otherwise an
 // offset into a base passed at launch: the per-step buffers, and the activation

@@ -30,8 +30,9 @@ struct Spec {
   static constexpr int KBD = KBD_;         // kblocks of K = intermediate (0: generic)
 };
 
-// A row of KB kblocks -> (kblocks per segment, segments, rows in flight): 8 or 14
-// loads of 16 bytes in flight per lane.  Other row lengths take the generic path.
+// A row of KB kblocks -> (kblocks per segment, segments, rows in flight): 8 to 16
+// loads of 16 bytes in flight per lane (a two-row ring for 8-kblock rows holds a whole
+// 16-row tile of a 4096-wide matrix).  Other row lengths take the generic path.
 constexpr bool kb_compiled(int KB) { return KB == 1 || KB == 2 || KB == 4 || KB == 8 || KB == 16 || KB == 28; }
 
 template <int BM, bool BF16, int KB>
@@ -39,7 +40,7 @@ __device__ __forceinline__ void gemv_kb(const LaunchArgs& a, const mk_task_t& d,
   if constexpr (KB == 1) gemv_run<BM, BF16, 1, 1, 8>(a, d, t, sm);
   else if constexpr (KB == 2) gemv_run<BM, BF16, 2, 1, 4>(a, d, t, sm);
   else if constexpr (KB == 4) gemv_run<BM, BF16, 4, 1, 2>(a, d, t, sm);
-  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 1>(a, d, t, sm);
+  else if constexpr (KB == 8) gemv_run<BM, BF16, 8, 1, 2>(a, d, t, sm);
   else if constexpr (KB == 16) gemv_run<BM, BF16, 8, 2, 1>(a, d, t, sm);
   else if constexpr (KB == 28 && BM == 1) gemv_run<BM, BF16, 14, 2, 1>(a, d, t, sm);
   else if constexpr (KB == 28) gemv_run<BM, BF16, 7, 4, 1>(a, d, t, sm);

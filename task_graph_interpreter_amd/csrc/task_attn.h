@@ -185,6 +185,65 @@ __device__ __forceinline__ void partial_merge(const LaunchArgs& a, Smem& sm, boo
   }
 }
 
+// The same log-sum-exp merge for the matrix-core pass, whose states come as kpw row
+// groups per wave that share the wave's maximum: lane l of wave w holds o[h][0 .. 8)
+// of row group l / lpk at dims 8 (l % lpk) (lpk = 64 / kpw lanes per row group), and
+// every lane holds the wave's (m[h], l[h]).  Each row group writes its o and lane 0
+// the wave's (m, l); after one barrier each thread finishes one output element: the
+// head's maximum M over the kWaves waves, one weight e^(m_w - M) per wave, applied
+// to the sum of that wave's row groups.
+template <int HM>
+__device__ __forceinline__ void partial_merge_rg(Smem& sm, bool first, int hc, int hd, int kpw, const float (&m)[HM],
+                                                 const float (&l)[HM], const float (&o)[HM][8], float* out,
+                                                 size_t out0, int stride) {
+  const int lane = lane_id(), wave = wave_id();
+  const int lpk = 64 / kpw, kl = lane / lpk, dl = lane % lpk;
+  // Staging: o as [kWaves * kpw][HM][hd], then (m, l) as [kWaves][HM][2].
+  float* po = sm.xs;
+  float* pml = po + (size_t)kWaves * kpw * HM * hd;
+  if (!first) __syncthreads();  // the previous pass may still read po / pml
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    if (h < hc) {
+      float* dst = po + ((size_t)(wave * kpw + kl) * HM + h) * hd + dl * 8;
+      *(f32x4*)dst = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+      *(f32x4*)(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      pml[(wave * HM + h) * 2] = m[h];
+      pml[(wave * HM + h) * 2 + 1] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < hc * hd; e += kThreads) {
+    const int h = e / hd, dd = e % hd;
+    float ms[kWaves];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      ms[w] = pml[(w * HM + h) * 2];
+      mx = fmaxf(mx, ms[w]);
+    }
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = ms[w] == -INFINITY ? 0.f : __expf(ms[w] - mx);  // every state empty: all 0
+      float ow = 0.f;
+      for (int k = 0; k < kpw; ++k) ow += po[((size_t)(w * kpw + k) * HM + h) * hd + dd];
+      acc = fmaf(wt, ow, acc);
+      lsum = fmaf(wt, pml[(w * HM + h) * 2 + 1], lsum);
+    }
+    st_dev<float>(out, out0 + h * stride + dd, acc);
+    if (dd == 0) {
+      st_dev<float>(out, out0 + h * stride + hd, mx);
+      st_dev<float>(out, out0 + h * stride + hd + 1, lsum);
+    }
+  }
+}
+
 // One pass over the chunk for query heads [hg, hg + HM) of the group; the first pass
 // (hg == 0) prefetches before waiting on the producers.
 template <bool BF16, int HM, int LPK, int R, bool BATCHED>
@@ -418,13 +477,15 @@ __device__ __forceinline__ bool partial_pass(const LaunchArgs& a, const mk_task_
 //    swaps and lane reads.
 //  * p = e^(s - m) goes through a 256-byte slice of LDS private to the wave to the
 //    lanes that hold the matching V rows (row groups of HD / 8 lanes, 16 bytes each,
-//    as in the pass above), which accumulate o[head][dims] += p v.  Those lanes'
-//    (m, l, o) are the states the merge combines (l counted once per wave).
+//    as in the pass above), which accumulate o[head][dims] += p v.  Those row
+//    groups' o, with the wave's (m, l), are the states partial_merge_rg combines.
+//  * The query rows are staged once into LDS after the wait (two waves' global-to-LDS
+//    loads), and every wave builds its B operand from there.
 //  * A ring of NS blocks of K and V is held in registers, loaded before the
-//    dependency wait and refilled in place after each block is folded.  The new
-//    token's row is masked in the ring (it is stale until APPEND has run); wave 0
-//    reads it with device-scope loads after the wait and folds it first, as a block
-//    holding only that row.
+//    dependency wait and refilled in place after each block is folded (no refill
+//    past the wave's last block).  The new token's row is masked in the ring (it is
+//    stale until APPEND has run); wave 0 reads it with device-scope loads after the
+//    wait and folds it first, as a block holding only that row.
 template <int HD, int NS>
 __device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm,
                                                   int hg) {
@@ -491,29 +552,6 @@ __device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_
       return false;
     }
   }
-  // B operand: column qc = head qc of the pass (zero past hc and for columns >= HM),
-  // dims 32 e + 8 g4 .. +8, scaled by 1/sqrt(HD) and split into bf16 hi and lo.
-  const float scale = 1.0f / sqrtf((float)HD);
-  bf16x8 qh[KS], ql[KS];
-#pragma unroll
-  for (int e = 0; e < KS; ++e) {
-    float qv[8];
-    if (qc < hc) {
-      const size_t q4 = ((size_t)b * Hq * HD + (size_t)(h0 + hg + qc) * HD + 32 * e + 8 * g4) / 4;
-      const f32x4 q0 = ld_dev_f4(qrot, q4), q1 = ld_dev_f4(qrot, q4 + 1);
-      qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w; qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) qv[u] = 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float v = qv[u] * scale;
-      const __bf16 h = (__bf16)v;
-      qh[e][u] = h;
-      ql[e][u] = (__bf16)(v - (float)h);
-    }
-  }
   // The new token's row (written by this step's APPEND), wave 0 only: K in the
   // score layout (lanes of key 0), V in the row layout (lanes of row 0).
   const bool has_new = jnew >= 0 && jnew < n;
@@ -529,6 +567,42 @@ __device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_
       for (int e = 0; e < KS; ++e) knew[e] = ld_dev_u4(kc, rn + 4 * e + g4);
     }
     if (kv == 0) vnew[0] = ld_dev_u4(vc, rn + dl);
+  }
+  // The pass's rotated query rows (hc x HD fp32, contiguous) are staged once into LDS
+  // by waves 1 and 2 with device-scope global-to-LDS loads (every wave needs all of
+  // them; eight waves loading the same bytes queue behind one another).
+  float* qs = sm.red + 512;  // [hc][HD]; the p slices use sm.red[0 .. 512)
+  if (wave == 1 || wave == 2) {
+    const int p = (wave - 1) * 64 + lane;  // 16-byte piece
+    if (p < hc * HD / 4)
+      __builtin_amdgcn_global_load_lds(
+          (const MK_GLOBAL void*)((const MK_GLOBAL f32x4*)qrot + ((size_t)b * Hq + h0 + hg) * (HD / 4) + p),
+          (__attribute__((address_space(3))) void*)(qs + (wave - 1) * 256), 16, 0, kCachePolicySC1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
+  }
+  __syncthreads();
+  // B operand: column qc = head qc of the pass (zero past hc and for columns >= HM),
+  // dims 32 e + 8 g4 .. +8, scaled by 1/sqrt(HD) and split into bf16 hi and lo.
+  const float scale = 1.0f / sqrtf((float)HD);
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int e = 0; e < KS; ++e) {
+    float qv[8];
+    if (qc < hc) {
+      const f32x4* qp = (const f32x4*)(qs + qc * HD + 32 * e + 8 * g4);
+      const f32x4 q0 = qp[0], q1 = qp[1];
+      qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w; qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qv[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = qv[u] * scale;
+      const __bf16 h = (__bf16)v;
+      qh[e][u] = h;
+      ql[e][u] = (__bf16)(v - (float)h);
+    }
   }
   float m = -INFINITY, l = 0.f;  // score layout: head qc; l over this lane's keys
   float o[HM][8];
@@ -606,26 +680,27 @@ __device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_
       const int i = i0 + s;
       if (i < nbw) block(kr[s], vr[s], 16 * (wave + kWaves * i), -1);
       __builtin_amdgcn_sched_barrier(0);
+      if (i + NS < nbw) {
 #pragma unroll
-      for (int e = 0; e < KS; ++e) kr[s][e] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff(i + NS, e), 0, 0);
+        for (int e = 0; e < KS; ++e) kr[s][e] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff(i + NS, e), 0, 0);
 #pragma unroll
-      for (int j = 0; j < VJ; ++j) vr[s][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff(i + NS, j), 0, 0);
+        for (int j = 0; j < VJ; ++j) vr[s][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff(i + NS, j), 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   trace_mark(a, sm, 0);
-  // States for the merge: each V row group of the wave is a state; all share the
-  // wave's m, and the wave's l (summed over the score layout's key groups) is counted
-  // in row group 0 only.
+  // The merge's states: the wave's V row groups, which share its m; the wave's l is
+  // summed over the score layout's key groups.
   float lt = l + lane_xor<16>(l);
   lt += lane_xor<32>(lt);
   float mh[HM], lh[HM];
 #pragma unroll
   for (int h = 0; h < HM; ++h) {
     mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), h));
-    lh[h] = kv == 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), h)) : 0.f;
+    lh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), h));
   }
-  partial_merge<HM, VEC>(a, sm, first, hc, HD, KPV, mh, lh, o, out, out0, stride);
+  partial_merge_rg<HM>(sm, first, hc, HD, KPV, mh, lh, o, out, out0, stride);
   return true;
 }
 

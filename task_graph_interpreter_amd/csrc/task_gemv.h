@@ -41,8 +41,6 @@ constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
 // The wave that waits for a tile's producers and stages its input (it streams its own
 // rows too).
 constexpr int kCtrlWave = kWaves - 1;
-// Cache-policy operand of a device-scope (sc1) load.
-constexpr int kCachePolicySC1 = 16;
 // s_waitcnt operand: vector memory counter 0, the others unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
