@@ -19,15 +19,20 @@
 //
 // Work split.  The weight rows of the tile are cut into blocks of 16 (SILU_MUL: gate
 // and up blocks interleaved, so a pair stays in one group), processed in groups of G
-// (8, 4, 2, 1).  K is cut into chunks of 256.  The workgroup's waves specialise, because
+// slots (8 slots for 5..8 blocks, 4 for 3..4, then 2, 1; every group restages the
+// whole input, so a tile runs as few groups as it can, and the empty slots of a group
+// load zeros without touching memory).  K is cut into chunks of 256.  The workgroup's
+// waves specialise, because
 // a wave's loads complete in issue order: a wave that loaded both weights and input
 // would drain its whole weight ring every time it waited for an input chunk.
 //  * Compute waves 0-3: wave w owns k-steps 2w and 2w + 1 (32 k each) of every chunk,
 //    for every block of the group.  A ring of 8 / G chunks of weight loads per block
 //    is in flight per lane (started before the dependency wait for the first group).
 //  * Staging waves 4-7 load input chunks two ahead into registers, scale by gamma,
-//    split into bf16 hi and lo, and write them to one of three LDS buffers,
-//    accumulating x^2 per batch row for the RMS scale.
+//    split into bf16 hi and lo (the hardware pair conversion, round to nearest even),
+//    and write them to one of three LDS buffers, accumulating x^2 per batch row for the
+//    RMS scale; tiles without the norm compile neither the gamma product nor the sums.
+//    The staging VALU work is what bounds these tiles.
 //  * One workgroup barrier per chunk.  A buffer is rewritten one chunk after the
 //    compute waves last read it (the barrier in between orders the two).
 // After the last chunk, the four compute waves' partial sums are added in LDS in a
@@ -38,6 +43,8 @@
 // following one agent-scope acquire: the 32 CUs of an XCD then share it through their
 // L2.
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -65,21 +72,45 @@ __device__ __forceinline__ int mfma_block_row(const MfmaGeom& g, int gb) {
   return g.c0 + 16 * (gb >> 1) + ((gb & 1) ? g.I : 0);
 }
 
-// One lane's 16 bytes of A for block gb, chunk c, k-step s (0..7): row-major, lane l
-// reads row l % 16 at k = 256 c + 32 s + 8 (l / 16); in the tile layout the k-step's
-// 1 KB tile of the block sits at 1024 (8 c + s), lane l's bytes at 16 l (the same
-// values).  Byte offsets < 4 GiB (checked when lowering).
-__device__ __forceinline__ u32x4 mfma_wload(const MfmaGeom& g, int gb, int c, int s, int lane) {
-  const uint32_t row0 = (uint32_t)mfma_block_row(g, gb);
-  uint32_t off;
-  if (g.packed) {
-    off = row0 * g.K * 2u + ((uint32_t)c * (kMfmaKC / 32) + (uint32_t)s) * 1024u + 16u * (uint32_t)lane;
-  } else {
-    const uint32_t row = row0 + (uint32_t)(lane & 15);
-    const uint32_t k = (uint32_t)c * kMfmaKC + (uint32_t)s * 32u + 8u * (uint32_t)(lane >> 4);
-    off = (row * g.K + k) * 2u;
-  }
-  return __builtin_nontemporal_load((const MK_GLOBAL u32x4*)((const MK_GLOBAL char*)g.W + off));
+// One lane's 16 bytes of A for a block whose first row starts at byte `blk` of the
+// matrix, chunk c, k-step s (0..7).  Both layouts give the block's base (first row
+// times 2K) + a per-lane term + c and s times per-chunk and per-step strides:
+//  * row-major: lane l reads row l % 16 at k = 256 c + 32 s + 8 (l / 16): lane term
+//    2K (l % 16) + 16 (l / 16), strides 512 and 64 bytes;
+//  * tile layout: the k-step's 1 KB tile of the block sits at 1024 (8 c + s), lane l's
+//    bytes at 16 l: lane term 16 l, strides 8192 and 1024 bytes (the same values).
+// A raw buffer load with a 32-bit offset (offsets < 4 GiB, checked when lowering):
+// no per-load layout branch or 64-bit address arithmetic, so the ring fill issues its
+// loads back to back instead of waiting on values the compiler had spilled.
+struct MfmaWAddr {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t lterm, cstride, sstride;
+};
+
+// The resource's range is the matrix's bytes (rows = the tile's N, or gate and up
+// rows with SiLU): a block slot with no block points at the end, so its loads fall
+// out of range and read zeros without a memory access.
+__device__ __forceinline__ uint32_t mfma_matrix_bytes(const MfmaGeom& g, const mk_task_t& d) {
+  const uint32_t rows = g.silu ? 2u * (uint32_t)g.I : (uint32_t)d.n;
+  return rows * g.K * 2u;
+}
+
+__device__ __forceinline__ MfmaWAddr mfma_waddr(const MfmaGeom& g, int lane, uint32_t range) {
+  MfmaWAddr w;
+  w.rs = __builtin_amdgcn_make_buffer_rsrc((void*)g.W, (short)0, (int)range, kRawBufferWord3);
+  w.lterm = g.packed ? 16u * (uint32_t)lane : 2u * g.K * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4);
+  w.cstride = g.packed ? 8192u : 512u;
+  w.sstride = g.packed ? 1024u : 64u;
+  return w;
+}
+
+__device__ __forceinline__ uint32_t mfma_blk(const MfmaGeom& g, int gb) {
+  return (uint32_t)mfma_block_row(g, gb) * g.K * 2u;
+}
+
+__device__ __forceinline__ u32x4 mfma_wload(const MfmaWAddr& wa, uint32_t blk, int c, int s) {
+  return __builtin_amdgcn_raw_buffer_load_b128(wa.rs, blk + wa.lterm + (uint32_t)c * wa.cstride + (uint32_t)s * wa.sstride,
+                                               0, kCachePolicyNT);
 }
 
 // Input chunk c of batch rows [b0, b0 + 32), as loaded by one staging thread st
@@ -109,34 +140,38 @@ __device__ __forceinline__ void mfma_xload(__amdgpu_buffer_rsrc_t xr, const char
   xr_out.gm = ldg<u32x2>(gamma, (size_t)c * (kMfmaKC / 4) + (st & 63));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+// Two floats rounded to bf16 (nearest even) and packed, the first in the low half.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
 }
 
 // Writes u = x * gamma into LDS buffer `xb` as bf16 hi and lo parts and, if `count`,
 // adds x^2 into ss (pre-gamma; the RMS scale multiplies the finished dot product).
-// Staging wave w' holds rows w' + 4 i.
-__device__ __forceinline__ void mfma_xstage(const XChunk& xr, bool norm, bool count, int B, int b0, int st,
+// Without the norm (NORM false) u = x and no sum is kept.  Staging wave w' holds rows
+// w' + 4 i; rows past the batch are written as zeros (`full`: none is).
+template <bool NORM>
+__device__ __forceinline__ void mfma_xstage(const XChunk& xr, bool count, bool full, int B, int b0, int st,
                                             uint16_t* xb, float ss[8]) {
-  const float g0 = norm ? bf16_lo(xr.gm.x) : 1.f, g1 = norm ? bf16_hi(xr.gm.x) : 1.f;
-  const float g2 = norm ? bf16_lo(xr.gm.y) : 1.f, g3 = norm ? bf16_hi(xr.gm.y) : 1.f;
+  const float g0 = NORM ? bf16_lo(xr.gm.x) : 1.f, g1 = NORM ? bf16_hi(xr.gm.x) : 1.f;
+  const float g2 = NORM ? bf16_lo(xr.gm.y) : 1.f, g3 = NORM ? bf16_hi(xr.gm.y) : 1.f;
   // Row st / 64 + 4 i, element 4 (st % 64): one base address, compile-time offsets.
   uint16_t* base = xb + (st >> 6) * kMfmaXPitch + 4 * (st & 63);
   const int br0 = b0 + (st >> 6);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     f32x4 v = xr.v[i];
-    if (br0 + 4 * i >= B) v = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float q = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
-    ss[i] += count ? q : 0.f;
-    const float u0 = v.x * g0, u1 = v.y * g1, u2 = v.z * g2, u3 = v.w * g3;
-    const uint16_t h0 = f32_to_bf16_rne(u0), h1 = f32_to_bf16_rne(u1);
-    const uint16_t h2 = f32_to_bf16_rne(u2), h3 = f32_to_bf16_rne(u3);
-    u32x2 hi, lo;
-    hi.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-    lo.x = pack_bf16x2(u0 - __uint_as_float((uint32_t)h0 << 16), u1 - __uint_as_float((uint32_t)h1 << 16));
-    lo.y = pack_bf16x2(u2 - __uint_as_float((uint32_t)h2 << 16), u3 - __uint_as_float((uint32_t)h3 << 16));
+    if (!full && br0 + 4 * i >= B) v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (NORM) {
+      const float q = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+      ss[i] += count ? q : 0.f;
+    }
+    const float u0 = NORM ? v.x * g0 : v.x, u1 = NORM ? v.y * g1 : v.y;
+    const float u2 = NORM ? v.z * g2 : v.z, u3 = NORM ? v.w * g3 : v.w;
+    // Round to nearest even with the hardware pair conversion (v_cvt_pk_bf16_f32).
+    const u32x2 hi = {cvt_bf16x2(u0, u1), cvt_bf16x2(u2, u3)};
+    const u32x2 lo = {cvt_bf16x2(u0 - bf16_lo(hi.x), u1 - bf16_hi(hi.x)),
+                      cvt_bf16x2(u2 - bf16_lo(hi.y), u3 - bf16_hi(hi.y))};
     *(u32x2*)(base + 4 * i * kMfmaXPitch) = hi;
     *(u32x2*)(base + kMfmaXHalf + 4 * i * kMfmaXPitch) = lo;
   }
@@ -151,11 +186,14 @@ __device__ __forceinline__ f32x4 mfma_step(const u32x4 a, const uint16_t* xb, in
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
 }
 
-// One group of G blocks [gb0, gb0 + G) over all K for batch rows [b0, b0 + 32).
-// Returns false if the step was abandoned while waiting.
+// One group of G block slots, the first nreal of them blocks [gb0, gb0 + nreal), over
+// all K for batch rows [b0, b0 + 32): each group restages the whole input, so a tile
+// runs as few groups as possible.  Slots past nreal load through a buffer resource of
+// range 0 (zeros, no memory access) and are not written.  Returns false if the step
+// was abandoned while waiting.
 template <int G>
 __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm,
-                                           const MfmaGeom& g, int gb0, int b0, bool first, const float* x,
+                                           const MfmaGeom& g, int gb0, int nreal, int b0, bool first, const float* x,
                                            const char* aux, float* y, bool need_ss) {
   constexpr int D = 8 / G;           // chunks of weight loads in flight per block (2 k-steps each)
   constexpr int U = D < 2 ? 2 : D;   // chunk loop unroll: ring slot and input register set are static
@@ -180,14 +218,18 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
   // of barriers: the dependency wait's, one after the first input chunks are staged,
   // one per chunk, and one before the partial sums are written.
   if (compute) {
+    const uint32_t range = mfma_matrix_bytes(g, d);
+    const MfmaWAddr wad = mfma_waddr(g, lane, range);
+    uint32_t blk[G];  // byte offset of each block's first row (wave-uniform); past the end if none
+#pragma unroll
+    for (int r = 0; r < G; ++r) blk[r] = r < nreal ? mfma_blk(g, gb0 + r) : range;
     u32x4 ring[D][G][2];
 #pragma unroll
     for (int dc = 0; dc < D; ++dc)
 #pragma unroll
       for (int r = 0; r < G; ++r)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          ring[dc][r][j] = mfma_wload(g, gb0 + r, dc < g.nc ? dc : g.nc - 1, 2 * w + j, lane);
+        for (int j = 0; j < 2; ++j) ring[dc][r][j] = mfma_wload(wad, blk[r], dc < g.nc ? dc : g.nc - 1, 2 * w + j);
     if (first) {
       if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
       // The input is read with plain loads: drop stale L1/L2 lines first.
@@ -210,7 +252,7 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const u32x4 wa = ring[dc % D][r][j];
-              ring[dc % D][r][j] = mfma_wload(g, gb0 + r, cn, 2 * w + j, lane);
+              ring[dc % D][r][j] = mfma_wload(wad, blk[r], cn, 2 * w + j);
               acc[r][0] = mfma_step(wa, xc, 0, 2 * w + j, lane, acc[r][0]);
               acc[r][1] = mfma_step(wa, xc, 1, 2 * w + j, lane, acc[r][1]);
             }
@@ -230,47 +272,55 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
       if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
       __syncthreads();
     }
-    float ss[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    XChunk xa, xb2;  // the next two input chunks to stage
-    mfma_xload(xrs, gamma, g.K, B, b0, 0, st, xa);
-    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 1 ? 1 : 0, st, xb2);
-    mfma_xstage(xa, norm, true, B, b0, st, xbuf, ss);
-    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 2 ? 2 : g.nc - 1, st, xa);
-    mfma_xstage(xb2, norm, g.nc > 1, B, b0, st, xbuf + kMfmaXBuf, ss);
-    mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 3 ? 3 : g.nc - 1, st, xb2);
-    __syncthreads();  // the first input chunks are staged
-    for (int c0 = 0; c0 < g.nc; c0 += U) {
+    const bool full = b0 + 32 <= B;  // every staged row is a batch row
+    // The staging loop, with the norm's gamma product and sums of squares compiled in
+    // only where the tile has the norm.
+    auto stage_all = [&](auto norm_c) __attribute__((always_inline)) {
+      constexpr bool NORM = decltype(norm_c)::value;
+      float ss[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      XChunk xa, xb2;  // the next two input chunks to stage
+      mfma_xload(xrs, gamma, g.K, B, b0, 0, st, xa);
+      mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 1 ? 1 : 0, st, xb2);
+      mfma_xstage<NORM>(xa, true, full, B, b0, st, xbuf, ss);
+      mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 2 ? 2 : g.nc - 1, st, xa);
+      mfma_xstage<NORM>(xb2, g.nc > 1, full, B, b0, st, xbuf + kMfmaXBuf, ss);
+      mfma_xload(xrs, gamma, g.K, B, b0, g.nc > 3 ? 3 : g.nc - 1, st, xb2);
+      __syncthreads();  // the first input chunks are staged
+      for (int c0 = 0; c0 < g.nc; c0 += U) {
 #pragma unroll
-      for (int dc = 0; dc < U; ++dc) {
-        const int c = c0 + dc;
-        if (c < g.nc) {
-          // Stage chunk c + 2 into the buffer chunk c - 1 used (every compute wave
-          // finished chunk c - 1 before the previous barrier), then load chunk c + 4
-          // into the freed registers.  Chunks past the end re-stage the last one into
-          // an idle buffer and are not counted in ss.
-          XChunk& xs = (dc & 1) ? xb2 : xa;  // c0 is even
-          mfma_xstage(xs, norm, c + 2 < g.nc, B, b0, st, xbuf + ((c + 2) % kMfmaXBufs) * kMfmaXBuf, ss);
-          mfma_xload(xrs, gamma, g.K, B, b0, c + 4 < g.nc ? c + 4 : g.nc - 1, st, xs);
-          __syncthreads();
+        for (int dc = 0; dc < U; ++dc) {
+          const int c = c0 + dc;
+          if (c < g.nc) {
+            // Stage chunk c + 2 into the buffer chunk c - 1 used (every compute wave
+            // finished chunk c - 1 before the previous barrier), then load chunk c + 4
+            // into the freed registers.  Chunks past the end re-stage the last one
+            // into an idle buffer and are not counted in ss.
+            XChunk& xs = (dc & 1) ? xb2 : xa;  // c0 is even
+            mfma_xstage<NORM>(xs, c + 2 < g.nc, full, B, b0, st, xbuf + ((c + 2) % kMfmaXBufs) * kMfmaXBuf, ss);
+            mfma_xload(xrs, gamma, g.K, B, b0, c + 4 < g.nc ? c + 4 : g.nc - 1, st, xs);
+            __syncthreads();
+          }
         }
       }
-    }
-    // Sum of squares of each staged batch row, kept in LDS for every group of this
-    // batch block (first group only: later groups restage the same rows).  Staging
-    // wave w' holds rows w' + 4 i, each lane one float4 of every chunk.
-    if (need_ss) {
+      // Sum of squares of each staged batch row, kept in LDS for every group of this
+      // batch block (first group only: later groups restage the same rows).  Staging
+      // wave w' holds rows w' + 4 i, each lane one float4 of every chunk.
+      if (NORM && need_ss) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float s = wave_sum(ss[i]);
-        if (lane == 0) row_ss[(w - kMfmaComputeWaves) + 4 * i] = s;
+        for (int i = 0; i < 8; ++i) {
+          const float s = wave_sum(ss[i]);
+          if (lane == 0) row_ss[(w - kMfmaComputeWaves) + 4 * i] = s;
+        }
       }
-    }
+    };
+    if (norm) stage_all(std::true_type{});
+    else stage_all(std::false_type{});
     __syncthreads();  // every wave is done with the staged input; partial sums reuse it
   }
   __syncthreads();
 
-  // Epilogue: element e = (pair or block, row 0..15, batch 0..31).
-  const int per = g.silu ? G / 2 : G;
+  // Epilogue: element e = (pair or block, row 0..15, batch 0..31), real blocks only.
+  const int per = g.silu ? nreal / 2 : nreal;
   for (int e = threadIdx.x; e < per * 512; e += kThreads) {
     const int q = e >> 9, rem = e & 511, rho = rem >> 5, bb = rem & 31;
     const int b = b0 + bb;
@@ -319,17 +369,19 @@ __device__ __forceinline__ void gemv_mfma(const LaunchArgs& a, const mk_task_t& 
     for (int gb0 = 0; gb0 < R;) {
       const int left = R - gb0;
       bool ok;
-      if (left >= 8) {
-        ok = mfma_group<8>(a, d, t, sm, g, gb0, b0, first, x, aux, y, need_ss);
-        gb0 += 8;
-      } else if (left >= 4) {
-        ok = mfma_group<4>(a, d, t, sm, g, gb0, b0, first, x, aux, y, need_ss);
-        gb0 += 4;
-      } else if (left >= 2) {
-        ok = mfma_group<2>(a, d, t, sm, g, gb0, b0, first, x, aux, y, need_ss);
+      // Groups of 8 slots take 5..8 blocks, of 4 take 3..4 (with SiLU the count is even).
+      if (left >= 5) {
+        const int nr = left < 8 ? left : 8;
+        ok = mfma_group<8>(a, d, t, sm, g, gb0, nr, b0, first, x, aux, y, need_ss);
+        gb0 += nr;
+      } else if (left >= 3) {
+        ok = mfma_group<4>(a, d, t, sm, g, gb0, left, b0, first, x, aux, y, need_ss);
+        gb0 += left;
+      } else if (left == 2) {
+        ok = mfma_group<2>(a, d, t, sm, g, gb0, 2, b0, first, x, aux, y, need_ss);
         gb0 += 2;
       } else {
-        ok = mfma_group<1>(a, d, t, sm, g, gb0, b0, first, x, aux, y, need_ss);
+        ok = mfma_group<1>(a, d, t, sm, g, gb0, 1, b0, first, x, aux, y, need_ss);
         gb0 += 1;
       }
       if (!ok) return;
