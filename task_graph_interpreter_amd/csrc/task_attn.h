@@ -517,7 +517,9 @@ __device__ __forceinline__ bool partial_pass_mfma(const LaunchArgs& a, const mk_
   const int jnew = pos - lo;  // the new token's key (if inside this chunk)
   const bool first = hg == 0;
 
-  const int lane = lane_id(), wave = wave_id();
+  int lane = lane_id();
+  asm volatile("" : "+v"(lane));  // per-lane offsets are recomputed per task, not hoisted and spilled
+  const int wave = wave_id();
   const int qc = lane & 15, g4 = lane >> 4;       // score layout: head column, key group
   const int kv = lane / LPK, dl = lane % LPK;     // V layout: row in a load, dims dl * 8
   const int nblk = (n + 15) >> 4;

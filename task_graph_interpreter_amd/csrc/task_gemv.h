@@ -245,7 +245,11 @@ __device__ __forceinline__ int gemv_batch_pass(int K) {
 template <int BM, bool BF16, int KBT, int SEG, int RPG>
 __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d, uint32_t t, Smem& sm) {
   constexpr int KBS = KBT > 0 ? KBT : 1;
-  const int lane = lane_id();
+  int lane = lane_id();
+  // Opaque to the optimiser: the per-lane offsets below are recomputed in each task
+  // (a few instructions) instead of being hoisted out of the interpreter loop, where
+  // they were spilled and came back as a chain of dependent scratch loads.
+  asm volatile("" : "+v"(lane));
   const GemvGeom g = gemv_geom<BF16>(a, d, wave_id());
   const int KB = KBT > 0 ? KBT : (g.KC + 63) >> 6;
   const int N = d.n, B = d.m;

@@ -197,7 +197,9 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
                                            const char* aux, float* y, bool need_ss) {
   constexpr int D = 8 / G;           // chunks of weight loads in flight per block (2 k-steps each)
   constexpr int U = D < 2 ? 2 : D;   // chunk loop unroll: ring slot and input register set are static
-  const int lane = lane_id(), w = wave_id();
+  int lane = lane_id();
+  asm volatile("" : "+v"(lane));  // recomputed per task, not hoisted and spilled
+  const int w = wave_id();
   const bool compute = w < kMfmaComputeWaves;
   const int B = d.m, N = d.n;
   const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;

@@ -62,7 +62,9 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
                                                  const MfmaGeom& g, int gb0, bool first, const char* aux, float* y,
                                                  __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t xrs,
                                                  __amdgpu_buffer_rsrc_t grs, bool need_ss) {
-  const int lane = lane_id(), w = wave_id();
+  int lane = lane_id();
+  asm volatile("" : "+v"(lane));  // recomputed per task, not hoisted and spilled
+  const int w = wave_id();
   const int B = d.m, N = d.n;
   const bool norm = d.flags & MK_FLAG_RMS_NORM_INPUT;
   const bool resid = d.flags & MK_FLAG_ADD_RESIDUAL;
