@@ -285,38 +285,25 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
 #pragma unroll
     for (int b = 0; b < BM; ++b) park[b] = 0.f;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // nothing pending into LDS (ring already landed)
-    if (g.NQ > 0) {
-      const int iters_ring = (g.NQ + RPG - 1) / RPG;
-      for (int it = 0; it < iters_ring; ++it) {
+    // Short compiled rings: the last ring iteration refills nothing.  Its next-row
+    // refills would all fall past the wave's last row, and such loads still in flight
+    // at the end of the stream complete behind the workgroup's other loads and hold up
+    // the flush (1B: 0.792 -> 0.787 ms).  The same peel of the 8-kblock ring pushed the
+    // 8B kernel into spills, so longer rings keep the single loop.
+    if constexpr (KBT > 0 && SEG == 1 && KBS <= 4) {
+      auto iteration = [&](int it, auto refill_c) __attribute__((always_inline)) {
+        constexpr bool REFILL = decltype(refill_c)::value;
         const int q0 = it * RPG;
-        // Short rows: the compiler may keep the staged input in registers across rows.
-        // Long rows: an opaque offset keeps the LDS reads inside the loop instead of
-        // pinning 8 registers per kblock.
-        int xoff = 0;
-        if (KBS * SEG > 8) asm volatile("" : "+v"(xoff));
-        const float* xsr = sm.xs + xoff;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
           float acc[BM];
 #pragma unroll
           for (int b = 0; b < BM; ++b) acc[b] = 0.f;
-          if (KBT > 0) {
 #pragma unroll
-            for (int s = 0; s < SEG; ++s) {
-#pragma unroll
-              for (int kb = 0; kb < KBS; ++kb) {
-                const int chunk = (s * KBS + kb) * 64 + lane;
-                gemv_consume<BM, BF16>(buf[r][kb], xsr, g.K, chunk, chunk < g.KC, nb, acc);
-                if (s + 1 < SEG) buf[r][kb] = gemv_load(g, q0 + r, (s + 1) * KBS + kb, lane);
-                else buf[r][kb] = gemv_load(g, q0 + RPG + r, kb, lane);
-              }
-            }
-          } else {
-            for (int kb = 0; kb < KB; ++kb) {
-              const int chunk = kb * 64 + lane;
-              const u32x4 w = gemv_load(g, q0 + r, kb, lane);
-              gemv_consume<BM, BF16>(w, sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
-            }
+          for (int kb = 0; kb < KBS; ++kb) {
+            const int chunk = kb * 64 + lane;
+            gemv_consume<BM, BF16>(buf[r][kb], sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
+            if (REFILL) buf[r][kb] = gemv_load(g, q0 + RPG + r, kb, lane);
           }
           const int q = q0 + r;
 #pragma unroll
@@ -328,6 +315,58 @@ __device__ __forceinline__ void gemv_run(const LaunchArgs& a, const mk_task_t& d
           }
           if ((q & 63) == 63 && q + 1 < g.NQ)  // more than 64 rows per wave: flush now
             gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
+        }
+      };
+      if (g.NQ > 0) {
+        const int iters_ring = (g.NQ + RPG - 1) / RPG;
+        for (int it = 0; it + 1 < iters_ring; ++it) iteration(it, std::true_type{});
+        iteration(iters_ring - 1, std::false_type{});
+      }
+    } else {
+      if (g.NQ > 0) {
+        const int iters_ring = (g.NQ + RPG - 1) / RPG;
+        for (int it = 0; it < iters_ring; ++it) {
+          const int q0 = it * RPG;
+          // Short rows: the compiler may keep the staged input in registers across rows.
+          // Long rows: an opaque offset keeps the LDS reads inside the loop instead of
+          // pinning 8 registers per kblock.
+          int xoff = 0;
+          if (KBS * SEG > 8) asm volatile("" : "+v"(xoff));
+          const float* xsr = sm.xs + xoff;
+  #pragma unroll
+          for (int r = 0; r < RPG; ++r) {
+            float acc[BM];
+  #pragma unroll
+            for (int b = 0; b < BM; ++b) acc[b] = 0.f;
+            if (KBT > 0) {
+  #pragma unroll
+              for (int s = 0; s < SEG; ++s) {
+  #pragma unroll
+                for (int kb = 0; kb < KBS; ++kb) {
+                  const int chunk = (s * KBS + kb) * 64 + lane;
+                  gemv_consume<BM, BF16>(buf[r][kb], xsr, g.K, chunk, chunk < g.KC, nb, acc);
+                  if (s + 1 < SEG) buf[r][kb] = gemv_load(g, q0 + r, (s + 1) * KBS + kb, lane);
+                  else buf[r][kb] = gemv_load(g, q0 + RPG + r, kb, lane);
+                }
+              }
+            } else {
+              for (int kb = 0; kb < KB; ++kb) {
+                const int chunk = kb * 64 + lane;
+                const u32x4 w = gemv_load(g, q0 + r, kb, lane);
+                gemv_consume<BM, BF16>(w, sm.xs, g.K, chunk, chunk < g.KC, nb, acc);
+              }
+            }
+            const int q = q0 + r;
+  #pragma unroll
+            for (int b = 0; b < BM; ++b) {
+              if (b < nb) {
+                const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_dpp(acc[b])), 63));
+                park[b] = (lane == (q & 63)) ? v * rs[b] : park[b];
+              }
+            }
+            if ((q & 63) == 63 && q + 1 < g.NQ)  // more than 64 rows per wave: flush now
+              gemv_flush<BM>(g, park, q - 63, nb, resid, (const float*)aux, y, N, b0);
+          }
         }
       }
     }
