@@ -231,7 +231,7 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
 #pragma unroll
       for (int r = 0; r < G; ++r)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ring[dc][r][j] = mfma_wload(wad, blk[r], dc < g.nc ? dc : g.nc - 1, 2 * w + j);
+        for (int j = 0; j < 2; ++j) ring[dc][r][j] = mfma_wload(wad, dc < g.nc ? blk[r] : range, dc < g.nc ? dc : 0, 2 * w + j);
     if (first) {
       if (!dep_wait(a, t, d.remaining_deps, sm)) return false;
       // The input is read with plain loads: drop stale L1/L2 lines first.
@@ -248,13 +248,16 @@ __device__ __forceinline__ bool mfma_group(const LaunchArgs& a, const mk_task_t&
         const int c = c0 + dc;
         if (c < g.nc) {
           const uint16_t* xc = xbuf + (c % kMfmaXBufs) * kMfmaXBuf;
-          const int cn = c + D < g.nc ? c + D : g.nc - 1;
+          // Refills past the last chunk point past the matrix's range: they read
+          // nothing (no repeated loads of the last chunk).
+          const bool past = c + D >= g.nc;
+          const int cn = past ? 0 : c + D;
 #pragma unroll
           for (int r = 0; r < G; ++r) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const u32x4 wa = ring[dc % D][r][j];
-              ring[dc % D][r][j] = mfma_wload(wad, blk[r], cn, 2 * w + j);
+              ring[dc % D][r][j] = mfma_wload(wad, past ? range : blk[r], cn, 2 * w + j);
               acc[r][0] = mfma_step(wa, xc, 0, 2 * w + j, lane, acc[r][0]);
               acc[r][1] = mfma_step(wa, xc, 1, 2 * w + j, lane, acc[r][1]);
             }

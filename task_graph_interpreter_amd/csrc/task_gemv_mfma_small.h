@@ -37,6 +37,8 @@
 // LDS, and the epilogue (r_b, residual, SiLU * up) writes y.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "task_gemv_mfma.h"
 
@@ -119,7 +121,8 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   for (int r = 0; r < G; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
   // One k-step from ring slot dd (steps s0 + dd; the slot is refilled with s0 + dd + D).
-  auto step = [&](int dd, int s0) __attribute__((always_inline)) {
+  auto step = [&](int dd, int s0, auto refill_c) __attribute__((always_inline)) {
+    constexpr bool REFILL = decltype(refill_c)::value;
     const int sn = s0 + dd + D;
     // u = x gamma for this lane's 4 values (the sum of squares is of x itself).
     float u[4];
@@ -142,8 +145,10 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
 #pragma unroll
     for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(u[e]));
     __builtin_amdgcn_sched_barrier(0);
-    xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
-    gr[dd] = __builtin_amdgcn_raw_buffer_load_b64(grs, goff(sn), 0, 0);
+    if (REFILL) {
+      xr[dd] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff(sn), 0, 0);
+      gr[dd] = __builtin_amdgcn_raw_buffer_load_b64(grs, goff(sn), 0, 0);
+    }
     // hi = u with the low 16 bits cleared, lo = the same of the exact remainder u - hi;
     // v_perm packs the upper halves of two floats into one bf16 pair.  The lane splits
     // its own 4 values and swaps half with its partner (lane ^ 8): a hi lane keeps the
@@ -171,8 +176,9 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
       // The product first, then the refill of the same ring slot: the new load can
       // land in the registers the product has read, so the ring never needs copying.
       acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[dd][r]), bop, acc[r], 0, 0, 0);
-      wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, lterm, sstride, sn, nst), 0,
-                                                        kCachePolicyNT);
+      if (REFILL)
+        wr[dd][r] = __builtin_amdgcn_raw_buffer_load_b128(wrs, mfma_small_woff(g, gb0 + r, lterm, sstride, sn, nst), 0,
+                                                          kCachePolicyNT);
     }
     // Keep each step's loads in its own step: the scheduler would otherwise gather
     // them at the end of the unrolled body, where they all drain before the next.
@@ -180,11 +186,21 @@ __device__ __forceinline__ bool mfma_small_group(const LaunchArgs& a, const mk_t
   };
   // The first D steps run outside the loop: they leave the ring in the order the loop
   // refills it, so the wait counts at the loop head are exact on entry as well.
+  // The last D steps refill nothing (their refills would all fall past the last step,
+  // and loads still in flight at the end of the stream hold up the epilogue).
+  if (nst > D) {
 #pragma unroll
-  for (int dd = 0; dd < D; ++dd) step(dd, 0);
-  for (int s0 = D; s0 < nst; s0 += D) {
+    for (int dd = 0; dd < D; ++dd) step(dd, 0, std::true_type{});
+    int s0 = D;
+    for (; s0 + D < nst; s0 += D) {
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd) step(dd, s0);
+      for (int dd = 0; dd < D; ++dd) step(dd, s0, std::true_type{});
+    }
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) step(dd, s0, std::false_type{});
+  } else {
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) step(dd, 0, std::false_type{});
   }
   // Sum of squares of each batch row over this wave's segment: the hi and lo lanes of
   // the row's column pair in the four k-quarters hold every value once.
