@@ -147,6 +147,9 @@ MFMA_CASES = {
     "b3_ragged": dict(batch=3, kv_len=(128, 41, 97), n_q_heads=8, gemv_tiles=5, kv_chunk=24),
     # batch 40: a full block of 32 rows, then a block of 8
     "b40": dict(batch=40, kv_len=tuple(40 + 2 * i for i in range(40)), gemv_tiles=8, kv_chunk=32),
+    # 5 tiles per matmul: 6-7 blocks per qkv tile and 12-13 per lm_head tile, so groups
+    # of 8 slots run with 5-7 real blocks (the empty slots read nothing)
+    "b32_odd": dict(batch=32, kv_len=(128,) * 32, gemv_tiles=5, kv_chunk=32),
     # wider layers: 4 and 8 chunks of K, so the input staging and the weight ring run
     # in steady state (several chunks per group)
     "b32_wide": dict(batch=32, kv_len=(128,) * 32, hidden=1024, n_q_heads=16, n_kv_heads=4, intermediate=2048,
@@ -199,7 +202,7 @@ def test_pack_matrix_layout(rows, cols):
     assert np.array_equal(got, want.reshape(-1))
 
 
-@pytest.mark.parametrize("case", ["b8", "b8_wide", "b1", "b3_ragged", "b32", "b40", "b32_wide"])
+@pytest.mark.parametrize("case", ["b8", "b8_wide", "b1", "b3_ragged", "b32", "b40", "b32_wide", "b32_odd"])
 def test_tiny_mfma_packed_weights_bitwise_row_major(case):
     # The matrix-core tiles reading the tile layout (MK_LOWER_PACKED_WEIGHTS) do the
     # same products in the same order as with row-major weights: every activation and
