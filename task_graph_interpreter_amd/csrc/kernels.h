@@ -115,10 +115,11 @@ __device__ __forceinline__ uint32_t next_task(const LaunchArgs& a, uint32_t& pos
 
 // The persistent interpreter.  Tasks are fetched two ahead: while task i runs, the
 // descriptors of tasks i and i + 1 are in LDS and the id of task i + 2 is being
-// fetched (the claim's round trip, or the list read, and the descriptor fetch overlap
-// the current task).  Descriptors and ids rotate through three LDS slots, which is safe because
-// every iteration ends in a workgroup barrier and slot i + 2 is written only at the
-// end of iteration i.  In dynamic mode each workgroup makes exactly one failing claim
+// fetched (the claim's round trip, or the list read, overlaps the current task); the
+// descriptor of task i + 2 is copied into its LDS slot right after task i's release.
+// Descriptors and ids rotate through three LDS slots, which is safe because every
+// iteration ends in a workgroup barrier and slot i + 2 is written only at the end of
+// iteration i.  In dynamic mode each workgroup makes exactly one failing claim
 // per step, so the ticket counter advances by n_tasks + grid per step and never needs
 // a reset; a workgroup holding two claimed tasks runs them in claim order, so the
 // lowest unfinished task is always running.  Trace mode (a.trace != null) records
@@ -167,9 +168,19 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
       if (trace) t_end = clock100();
       if (status != 0) sm.stop = 1;
       sm.ticket[s2] = nn;
-      if (nn < a.n_tasks) stage_desc(a, nn, sm, s2);
     }
     release_dependents(a, d);
+    // Descriptor i + 2 is copied into its slot after the release (a load issued before
+    // it would hold the release up): lanes 0..3 of wave 0 each copy 16 bytes with a
+    // global-to-LDS load.  The next iteration's release waits for it and meets at a
+    // barrier, so the slot is complete before it is read two iterations on.
+    if (wave_id() == 0) {
+      const uint32_t ln = lane_id();
+      const uint32_t t2 = sm.ticket[s2];
+      if (ln < 4 && t2 < a.n_tasks)
+        __builtin_amdgcn_global_load_lds((const MK_GLOBAL void*)((const MK_GLOBAL u32x4*)a.tasks + (size_t)t2 * 4 + ln),
+                                         (__attribute__((address_space(3))) void*)&sm.desc[s2], 16, 0, 0);
+    }
     if (trace && threadIdx.x == 0) {
       const uint64_t t_rel = clock100();
       const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID
@@ -182,6 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void interpreter_kernel(LaunchArgs a) 
       for (int i = 0; i < 3; ++i) stg<uint64_t>(a.trace, 8ull * t + 5 + i, sm.t_mark[i]);
     }
   }
+  // A stop after an error can leave the last descriptor copy in flight.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // One launch per op: blockIdx.x = task within the op; stream order replaces the
